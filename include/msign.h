@@ -1,0 +1,191 @@
+/*
+ * msign.h - C ABI of libmsign, a HIP/CDNA4 (gfx950) library that computes
+ * msign(M) = (M M^T)^{-1/2} M = U V^T by Newton-Schulz iteration.
+ *
+ * Sources (cited by page title and section):
+ *   [KX] "msign算子的Newton-Schulz迭代（上）" (kexue.fm/archives/10922):
+ *        §写在前面 definition of msign; §迭代计算 the quintic iteration,
+ *        Frobenius normalisation and the constants (3.4445, -4.7750, 2.0315),
+ *        T = 5; §参考实现 batching over the last two dims, transpose when
+ *        rows > cols, eps = 1e-20; §解开约束 per-step coefficients.
+ *   [GR] "Gram Newton-Schulz" (zifeng-mai.github.io/2026/04/05/GramNewtonSchulz):
+ *        §2.3 Algorithm 1, §3.2 restarting, §3.3 fp16 and the a_t terms kept
+ *        out of Z, §3.4 Algorithm 2, §4 symmetric GEMM C <- aAB + bC + gI.
+ *   [NB] nil9.net, flash-muon excerpt: the X X^T operator that computes only
+ *        upper-triangle tiles and stores each tile's transpose into the
+ *        mirrored lower-triangle tile.
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: contiguous row-major [batch, rows, cols]; matrix b starts at
+ *     element b*rows*cols.  Pointers are DEVICE pointers unless stated.
+ *   - Ownership: the caller owns every buffer (inputs, outputs, workspace).
+ *     The library never allocates or frees device memory and keeps no
+ *     pointer after a call returns.  All work is queued on `stream` (0 is
+ *     the null stream); no call synchronises the host.
+ *   - Errors: arguments are validated on the host before anything is
+ *     launched; a non-OK status means nothing was launched and nothing
+ *     written.  MSIGN_ERR_HIP reports a failed launch; msign_last_error()
+ *     then holds the HIP message (thread-local).  No call aborts.
+ *   - Degenerate sizes: batch, rows or cols equal to 0 is a successful no-op.
+ *     NaN/Inf in the input propagate; an all-zero matrix maps to zero.
+ *   - Bit stability: results do not depend on timing (no atomics, fixed
+ *     reduction orders); the same call on the same device gives the same bits.
+ *   - Concurrency: calls are thread-safe and may run on different streams as
+ *     long as they do not share output or workspace buffers.
+ */
+#ifndef MSIGN_H_
+#define MSIGN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSIGN_F32 = 0,
+  MSIGN_BF16 = 1,
+  MSIGN_F16 = 2
+} msign_dtype_t;
+
+typedef enum {
+  MSIGN_OK = 0,
+  MSIGN_ERR_ARG = 1,        /* null pointer, bad steps/eps/restart list   */
+  MSIGN_ERR_DTYPE = 2,      /* unknown dtype or unsupported combination   */
+  MSIGN_ERR_SHAPE = 3,      /* negative or too large size                  */
+  MSIGN_ERR_WORKSPACE = 4,  /* workspace null or smaller than required     */
+  MSIGN_ERR_ALIAS = 5,      /* output partially overlaps input/workspace   */
+  MSIGN_ERR_HIP = 6         /* a HIP launch failed                         */
+} msign_status_t;
+
+/* Largest number of iteration steps accepted (coefficient tables). */
+#define MSIGN_MAX_STEPS 64
+
+/*
+ * Bytes of device workspace msign_ns needs for this problem.  Returns 0 for
+ * empty problems and (size_t)-1 for invalid sizes or dtypes.
+ */
+size_t msign_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
+                                int32_t compute_dtype);
+
+/*
+ * msign_ns - standard quintic Newton-Schulz ([KX] §迭代计算, §参考实现).
+ *
+ * For each matrix M (rows x cols) of the batch: X = M, or M^T when
+ * rows > cols (n = min(rows, cols), m = max); X0 = X / sqrt(sum X^2 + eps);
+ * then for t = 1..steps with (a_t, b_t, c_t):
+ *     A = X X^T;  B = b_t A + c_t A A;  X <- a_t X + B X
+ * and the result (transposed back when rows > cols) is written to y.
+ *
+ *   x, y           device, [batch, rows, cols] in io_dtype.  y == x (in place)
+ *                  is allowed; any other overlap of y with x or workspace is
+ *                  MSIGN_ERR_ALIAS.
+ *   io_dtype       MSIGN_F32, MSIGN_BF16 or MSIGN_F16 (input and output).
+ *   compute_dtype  operand dtype of the matrix products: MSIGN_BF16 or
+ *                  MSIGN_F16 (MFMA with fp32 accumulation) or MSIGN_F32 (fp32
+ *                  MFMA).  The iterate X itself is carried in fp32 between
+ *                  steps; A and B are stored in compute_dtype.
+ *   steps          1..MSIGN_MAX_STEPS.
+ *   coeffs         HOST pointer to steps*3 floats (a_t, b_t, c_t per row,
+ *                  [KX] §解开约束), or NULL for (3.4445, -4.7750, 2.0315)
+ *                  at every step.  Read before the call returns.
+ *   eps            >= 0, added to sum X^2 before the square root (1e-20 in
+ *                  [KX] §参考实现).
+ *   workspace      device, at least msign_ns_workspace_bytes(...) bytes,
+ *                  256-byte aligned, contents on entry irrelevant.
+ */
+msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows,
+                        int64_t cols, int32_t io_dtype, int32_t compute_dtype,
+                        int32_t steps, const float* coeffs, float eps,
+                        void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Bytes of device workspace msign_gram_ns needs; see msign_ns_workspace_bytes. */
+size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
+                                     int32_t compute_dtype);
+
+/*
+ * msign_gram_ns - Gram Newton-Schulz ([GR] §3.4 Algorithm 2; with no restart
+ * it is §2.3 Algorithm 1).
+ *
+ * X0 as in msign_ns, rounded to compute_dtype ([GR] §3.4 step 2).  Then
+ *     R = X X^T, Q = I; for t = 1..steps:
+ *         Z = b_t R + c_t R^2;  Q <- Q Z + a_t Q;
+ *         RZ = R Z + a_t R;     R <- Z RZ + a_t RZ    (skipped when unused)
+ *         after t in restart_after (t < steps): X <- Q X, R = X X^T, Q = I
+ *     y = Q X  (transposed back when rows > cols).
+ * Q, R, Z and RZ are n x n, kept exactly symmetric (upper-triangle tiles,
+ * mirrored).  The a_t terms are applied in fp32 epilogues ([GR] §3.3); the
+ * first Q of each block is Z + a_t I, added on the diagonal in registers.
+ *
+ *   compute_dtype   MSIGN_F16 (the pages' choice, [GR] §3.3), MSIGN_BF16 or
+ *                   MSIGN_F32.
+ *   restart_after   HOST array of n_restarts step indices, strictly
+ *                   increasing, each in 1..steps-1; NULL iff n_restarts == 0.
+ *                   Algorithm 2 uses {2}.
+ *   other arguments as in msign_ns.
+ */
+msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch,
+                             int64_t rows, int64_t cols, int32_t io_dtype,
+                             int32_t compute_dtype, int32_t steps,
+                             const float* coeffs, float eps,
+                             const int32_t* restart_after, int32_t n_restarts,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * syrk_xxt - C = alpha X X^T + beta D + gamma I for each matrix of a batch
+ * ([NB] X X^T operator; [GR] §4 fused form C <- aAB + bC + gI with A = X,
+ * B = X^T).
+ *
+ * Only upper-triangle tiles are computed; each is stored and its transpose
+ * is stored into the mirrored tile, so C is exactly (bitwise) symmetric.
+ *   x      device, [batch, n, k] in dtype (row pitch k).
+ *   c      device, [batch, n, n] in dtype.  Must not overlap x or d.
+ *   dtype  MSIGN_BF16 or MSIGN_F16 (MFMA, fp32 accumulation, one rounding on
+ *          store) or MSIGN_F32.
+ *   d      device, [batch, n, n] in dtype, or NULL (then beta is ignored).
+ *          D must be symmetric; its upper triangle is what is read.
+ *   workspace, workspace_bytes  device scratch of at least
+ *          syrk_xxt_workspace_bytes(...) bytes (0 bytes, NULL allowed, when
+ *          k is a multiple of 8 elements for bf16/f16 and of 4 for f32).
+ */
+size_t syrk_xxt_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t dtype);
+
+msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n,
+                        int64_t k, int32_t dtype, float alpha, const void* d,
+                        float beta, float gamma, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char* msign_status_string(msign_status_t status);
+
+/* Detail of the last non-OK status on the calling thread ("" if none). */
+const char* msign_last_error(void);
+
+/* Library version string, e.g. "msign 0.1.0 gfx950". */
+const char* msign_version(void);
+
+/*
+ * Per-kernel-class timing with HIP events, for measurement only.
+ * While enabled, every launch made by the calls above is bracketed by a pair
+ * of events recorded on the call's stream; msign_kernel_timing_read() waits
+ * for them, adds their durations to per-class totals and clears the queue.
+ * Classes: 0 = normalise (sum of squares + scale/cast), 1 = X X^T (triangle),
+ * 2 = n x n triangle products (A^2 / Gram R, Q, Z, RZ updates), 3 = the
+ * rectangular product (B X, Q X).
+ *   msign_kernel_timing_enable   1 enables, 0 disables (and frees events);
+ *                                returns MSIGN_ERR_HIP if events cannot be made.
+ *   msign_kernel_timing_read     fills total_ms[4] and launches[4] (HOST).
+ */
+#define MSIGN_KCLASS_COUNT 4
+msign_status_t msign_kernel_timing_enable(int32_t enable);
+msign_status_t msign_kernel_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSIGN_H_ */

@@ -1,0 +1,14 @@
+"""msign by Newton-Schulz iteration on MI355X (gfx950).
+
+Python face of libmsign (C ABI in include/msign.h).  The binding only
+marshals arguments; all computation runs in the HIP library, which must be
+built (`python -m msign_newton_schulz_amd.build`) before use.
+"""
+
+from ._binding import (F32, BF16, F16, LIB_PATH, MsignError, gram_ns_workspace_bytes,  # noqa: F401
+                       kernel_timing, library, msign_gram_ns, msign_ns, ns_workspace_bytes,
+                       read_kernel_timing, syrk_xxt, version)
+
+__all__ = ["msign_ns", "msign_gram_ns", "syrk_xxt", "MsignError", "library", "version",
+           "ns_workspace_bytes", "gram_ns_workspace_bytes", "kernel_timing", "read_kernel_timing",
+           "LIB_PATH", "F32", "BF16", "F16"]

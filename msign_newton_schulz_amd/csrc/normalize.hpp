@@ -1,0 +1,141 @@
+// Frobenius normalisation X0 = X / sqrt(sum X^2 + eps) ("msign算子的
+// Newton-Schulz迭代（上）" §迭代计算 and §参考实现), in two HBM-bound passes:
+//
+//  1. sumsq_partial_kernel: grid (nblk, batch).  Each block squares and sums
+//     one contiguous slice of one matrix in fp32 (16-byte loads when
+//     aligned), reduces across the block with a fixed shuffle tree and writes
+//     one partial.  Fixed slice boundaries and trees make the sum bit-stable.
+//  2. normalize_kernel: grid (64x64 tiles of the padded input, batch).  Each
+//     block re-sums that matrix's partials in a fixed order, forms the scale
+//     1/sqrt(sum + eps) in fp32, loads its input tile into LDS, and writes
+//     every requested copy of the scaled tile: in the input's orientation or
+//     transposed (read back column-wise from LDS so both stores coalesce), in
+//     fp32 or the compute dtype.  Tiles cover the padded extents, so padding
+//     rows and columns of every copy are written as zeros.
+//     A null partial pointer means scale 1 (a plain cast/transpose/pad).
+#pragma once
+
+#include "common.hpp"
+
+namespace msign {
+
+struct NormOut {
+  void* ptr;
+  int64_t ld;
+  int64_t bstride;
+  int32_t dtype;
+  int32_t transposed;  // relative to the input's orientation
+};
+
+struct NormParams {
+  const void* x;
+  int32_t x_dtype;
+  int64_t rows, cols;           // true input dims; batch stride rows * cols
+  int32_t rows_pad, cols_pad;   // extent covered (input orientation)
+  const float* partial;         // [batch][nblk] or null (scale 1)
+  int32_t nblk;
+  float eps;
+  NormOut out[3];
+  int32_t nout;
+};
+
+template <int NT>
+__global__ void __launch_bounds__(NT)
+sumsq_partial_kernel(const void* x, int32_t dt, int64_t count, int32_t nblk, float* partial) {
+  const int64_t b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int esz = dt == DT_F32 ? 4 : 2;
+  const char* base = static_cast<const char*>(x) + b * count * esz;
+  const int64_t chunk = (((count + nblk - 1) / nblk) + 7) & ~(int64_t)7;
+  const int64_t start = (int64_t)blockIdx.x * chunk;
+  const int64_t end = start + chunk < count ? start + chunk : count;
+
+  float s = 0.f;
+  if (start < end) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15) == 0;
+    int64_t done = start;
+    if (aligned) {
+      const int64_t nvec = (end - start) / 8;
+      for (int64_t v = tid; v < nvec; v += NT) {
+        const int64_t e = start + v * 8;
+        if (dt == DT_F32) {
+          const f32x4* pv = reinterpret_cast<const f32x4*>(base + e * 4);
+          f32x4 u = pv[0], w = pv[1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s += u[q] * u[q] + w[q] * w[q];
+        } else {
+          u32x4 u = *reinterpret_cast<const u32x4*>(base + e * 2);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint16_t lo = u[q] & 0xffff, hi = u[q] >> 16;
+            const float f0 = dt == DT_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
+            const float f1 = dt == DT_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
+            s += f0 * f0 + f1 * f1;
+          }
+        }
+      }
+      done = start + nvec * 8;
+    }
+    for (int64_t e = done + tid; e < end; e += NT) {
+      const float f = load_as_f32(base, e, dt);
+      s += f * f;
+    }
+  }
+  // fixed-order block reduction
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  __shared__ float ws[NT / 64];
+  if ((tid & 63) == 0) ws[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < NT / 64; ++w) t += ws[w];
+    partial[b * nblk + blockIdx.x] = t;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+normalize_kernel(const NormParams p) {
+  __shared__ float tile[64][65];
+  __shared__ float s_scale;
+  const int64_t b = blockIdx.z;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    float scale = 1.f;
+    if (p.partial != nullptr) {
+      float s = 0.f;
+      for (int i = tid; i < p.nblk; i += 64) s += p.partial[b * p.nblk + i];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+      scale = 1.0f / sqrtf(s + p.eps);
+    }
+    if (tid == 0) s_scale = scale;
+  }
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = tid & 63, ty = tid >> 6;
+  const int64_t xb = b * p.rows * p.cols;
+  for (int rr = ty; rr < 64; rr += 4) {
+    const int64_t r = r0 + rr, c = c0 + tx;
+    tile[rr][tx] = (r < p.rows && c < p.cols) ? load_as_f32(p.x, xb + r * p.cols + c, p.x_dtype) : 0.f;
+  }
+  __syncthreads();
+  const float sc = s_scale;
+  for (int o = 0; o < p.nout; ++o) {
+    const NormOut& os = p.out[o];
+    if (!os.transposed) {
+      for (int rr = ty; rr < 64; rr += 4) {
+        const int r = r0 + rr, c = c0 + tx;
+        if (r < p.rows_pad && c < p.cols_pad)
+          store_from_f32(os.ptr, b * os.bstride + (int64_t)r * os.ld + c, os.dtype, tile[rr][tx] * sc);
+      }
+    } else {
+      for (int cc = ty; cc < 64; cc += 4) {
+        const int c = c0 + cc, r = r0 + tx;
+        if (r < p.rows_pad && c < p.cols_pad)
+          store_from_f32(os.ptr, b * os.bstride + (int64_t)c * os.ld + r, os.dtype, tile[tx][cc] * sc);
+      }
+    }
+  }
+}
+
+}  // namespace msign

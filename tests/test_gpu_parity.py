@@ -1,0 +1,263 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Sizes here finish in seconds on the oracle yet span several 128x128 tiles
+and ragged tails.  Tolerances: max relative Frobenius error 2e-2 for bf16 and
+fp16 products and 1e-4 for fp32 products (against the oracle's NS output);
+exact bitwise checks for symmetry, batching and determinism.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from gpu_util import TORCH_DT, announce, f64, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f16": 2e-2, "f32": 1e-4}
+
+
+def _input(rows, cols, io, seed, batch=1, noise=1.0, spike=0):
+    return S.small_case(rows, cols, io, seed, batch=batch, noise_std=noise, spike_rank=spike)
+
+
+# --------------------------------------------------------------- syrk_xxt --
+
+SYRK_SHAPES = [(1, 8), (16, 64), (17, 33), (100, 300), (129, 257), (256, 512), (300, 64)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("n,k", SYRK_SHAPES)
+def test_syrk_matches_exact_product(dt, n, k):
+    M = require_gpu()
+    announce(f"syrk n={n} k={k} dt={dt}")
+    x = _input(n, k, dt, 500 + n + k, batch=2)
+    c = M.syrk_xxt(x.cuda())
+    torch.cuda.synchronize()
+    cc = f64(c)
+    xx = f64(x)
+    ref = xx @ np.swapaxes(xx, -1, -2)
+    absx = np.abs(xx)
+    scale = absx @ np.swapaxes(absx, -1, -2)
+    u = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -23}[dt]
+    bound = scale * (u + 2 * k * 2.0 ** -24) + 1e-30
+    assert np.all(np.abs(cc - ref) <= bound), float(np.max(np.abs(cc - ref) / bound))
+    ct = c.transpose(-1, -2).contiguous()
+    assert torch.equal(c, ct), "C must be bitwise symmetric"
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_syrk_fused_epilogue(dt):
+    M = require_gpu()
+    announce(f"syrk epilogue dt={dt}")
+    n, k = 200, 136
+    x = _input(n, k, dt, 42)
+    d0 = _input(n, n, dt, 43)
+    d = ((d0 + d0.transpose(-1, -2)) * 0.5).to(TORCH_DT[dt])  # symmetric
+    alpha, beta, gamma = 0.75, -1.5, 2.25
+    c = M.syrk_xxt(x.cuda(), alpha=alpha, d=d.cuda(), beta=beta, gamma=gamma)
+    torch.cuda.synchronize()
+    xx, dd = f64(x)[0], f64(d)[0]
+    ref = alpha * xx @ xx.T + beta * dd + gamma * np.eye(n)
+    scale = abs(alpha) * np.abs(xx) @ np.abs(xx).T + abs(beta) * np.abs(dd) + abs(gamma)
+    u = {"bf16": 2.0 ** -8, "f32": 2.0 ** -22}[dt]
+    assert np.all(np.abs(f64(c)[0] - ref) <= scale * (u + 2 * k * 2.0 ** -24))
+    assert torch.equal(c, c.transpose(-1, -2).contiguous())
+
+
+def test_syrk_deterministic_and_batched_equals_single():
+    M = require_gpu()
+    announce("syrk determinism")
+    x = _input(384, 1000, "bf16", 7, batch=3).cuda()
+    c1 = M.syrk_xxt(x)
+    c2 = M.syrk_xxt(x)
+    c_single = M.syrk_xxt(x[1:2].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert torch.equal(c1[1:2], c_single)
+
+
+def test_syrk_empty_k_gives_beta_d_plus_gamma():
+    M = require_gpu()
+    announce("syrk k=0")
+    x = torch.empty((1, 5, 0), dtype=torch.float32, device="cuda")
+    d = torch.eye(5, device="cuda").reshape(1, 5, 5) * 3
+    c = M.syrk_xxt(x, d=d, beta=2.0, gamma=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(c.cpu(), torch.eye(5).reshape(1, 5, 5) * 7)
+
+
+# ------------------------------------------------------------------ msign_ns --
+
+NS_CASES = [
+    # rows, cols, io, compute, batch
+    (128, 256, "f32", "f32", 1),    # the small fp32 workload
+    (128, 256, "f32", "bf16", 1),
+    (200, 70, "bf16", "bf16", 2),   # tall, ragged
+    (70, 200, "bf16", "bf16", 2),   # wide, ragged
+    (129, 129, "bf16", "f16", 1),   # square, ragged tail
+    (1, 37, "bf16", "bf16", 1),     # a vector
+    (37, 1, "f16", "f16", 1),
+    (96, 160, "f16", "bf16", 3),
+    (300, 520, "f32", "f32", 1),
+]
+
+
+@pytest.mark.parametrize("rows,cols,io,cdt,batch", NS_CASES)
+def test_ns_matches_oracle(rows, cols, io, cdt, batch):
+    M = require_gpu()
+    announce(f"msign_ns {batch}x{rows}x{cols} io={io} compute={cdt}")
+    x = _input(rows, cols, io, 1000 + rows * 7 + cols, batch=batch)
+    y = M.msign_ns(x.cuda(), compute_dtype=TORCH_DT[cdt])
+    torch.cuda.synchronize()
+    assert y.shape == x.shape and y.dtype == x.dtype
+    err = O.max_rel_fro_error(f64(y), O.ns(f64(x)))
+    assert err <= TOL[cdt], err
+
+
+def test_ns_small_fp32_workload_against_exact_and_oracle():
+    """The 128x256 fp32 workload: fp32 products match oracle NS to 1e-4, and
+    the oracle itself sits within the pages' bound of the exact U V^T."""
+    M = require_gpu()
+    gr = S.WORKLOADS["c1_128x256_f32"].groups[0]
+    announce("msign_ns 128x256 f32 workload")
+    x = S.group_batch(gr)
+    y = f64(M.msign_ns(x.cuda(), compute_dtype=torch.float32))
+    xs = f64(x)
+    assert O.max_rel_fro_error(y, O.ns(xs)) <= 1e-4
+    s = np.linalg.svd(xs[0], compute_uv=False)
+    bound = float(np.max(np.abs(O.phi(s / np.linalg.norm(s)) - 1)))
+    assert O.max_rel_fro_error(y, O.exact_msign(xs)) <= bound + 1e-4
+
+
+@pytest.mark.parametrize("cdt", ["bf16", "f16"])
+def test_ns_spiked_alpha4_workload(cdt):
+    """1024x4096 bf16, N(0, 0.02^2) + rank-8 spike (full size)."""
+    M = require_gpu()
+    gr = S.WORKLOADS["c2_1024x4096_bf16"].groups[0]
+    announce(f"msign_ns 1024x4096 spiked compute={cdt}")
+    x = S.group_batch(gr)
+    y = M.msign_ns(x.cuda(), compute_dtype=TORCH_DT[cdt])
+    torch.cuda.synchronize()
+    err = O.max_rel_fro_error(f64(y), O.ns(f64(x)))
+    assert err <= 2e-2, err
+
+
+def test_ns_per_step_coefficients_and_steps():
+    M = require_gpu()
+    announce("msign_ns per-step table T=6")
+    table = np.array([[3955, -8306, 5008], [3735, -6681, 3463], [3799, -6499, 3211],
+                      [4019, -6385, 2906], [2677, -3029, 1162], [2172, -1833, 682]]) / 1024.0
+    x = _input(160, 352, "f32", 77)
+    y = M.msign_ns(x.cuda(), steps=6, coeffs=table.tolist(), compute_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert O.max_rel_fro_error(f64(y), O.ns(f64(x), coeffs=table, steps=6)) <= 1e-4
+    y1 = M.msign_ns(x.cuda(), steps=1, compute_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert O.max_rel_fro_error(f64(y1), O.ns(f64(x), steps=1)) <= 1e-4
+
+
+def test_ns_bitwise_invariants():
+    M = require_gpu()
+    announce("msign_ns invariants")
+    x = _input(192, 320, "bf16", 5, batch=4).cuda()
+    y = M.msign_ns(x)
+    y_again = M.msign_ns(x)
+    y_one = M.msign_ns(x[2:3].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_again), "run to run"
+    assert torch.equal(y[2:3], y_one), "batched == single"
+    z = M.msign_ns(torch.zeros_like(x))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z).item() == 0
+    # in place
+    xc = x.clone()
+    M.msign_ns(xc, out=xc)
+    torch.cuda.synchronize()
+    assert torch.equal(xc, y)
+
+
+def test_ns_transpose_and_scale():
+    M = require_gpu()
+    announce("msign_ns transpose/scale")
+    x = _input(96, 224, "f32", 9)
+    y = f64(M.msign_ns(x.cuda(), compute_dtype=torch.float32))
+    yt = f64(M.msign_ns(x.transpose(-1, -2).contiguous().cuda(), compute_dtype=torch.float32))
+    ys = f64(M.msign_ns((x * 1024).cuda(), compute_dtype=torch.float32))
+    assert np.max(np.abs(yt - np.swapaxes(y, -1, -2))) <= 1e-5
+    assert np.max(np.abs(ys - y)) <= 1e-5
+
+
+def test_ns_nan_propagates():
+    M = require_gpu()
+    announce("msign_ns NaN input")
+    x = _input(64, 128, "bf16", 3)
+    x[0, 5, 7] = float("nan")
+    y = M.msign_ns(x.cuda())
+    torch.cuda.synchronize()
+    assert torch.isnan(y).any().item()
+
+
+def test_ns_empty_batch():
+    M = require_gpu()
+    x = torch.empty((0, 64, 128), dtype=torch.bfloat16, device="cuda")
+    assert M.msign_ns(x).shape == x.shape
+
+
+# ------------------------------------------------------------- msign_gram_ns --
+
+GRAM_CASES = [
+    # rows, cols, io, compute, restarts, batch
+    (128, 256, "f32", "f32", (2,), 1),
+    (128, 256, "f32", "f32", (), 1),
+    (128, 256, "f32", "f32", (1, 2, 3, 4), 1),
+    (96, 400, "bf16", "f16", (2,), 2),
+    (400, 96, "bf16", "f16", (2,), 2),     # tall
+    (130, 260, "f16", "f16", (), 1),
+    (130, 260, "bf16", "bf16", (2,), 1),
+    (1, 40, "f16", "f16", (2,), 1),
+]
+
+
+@pytest.mark.parametrize("rows,cols,io,cdt,restarts,batch", GRAM_CASES)
+def test_gram_matches_oracle_ns(rows, cols, io, cdt, restarts, batch):
+    M = require_gpu()
+    announce(f"msign_gram_ns {batch}x{rows}x{cols} io={io} compute={cdt} restarts={restarts}")
+    x = _input(rows, cols, io, 2000 + rows + cols, batch=batch)
+    y = M.msign_gram_ns(x.cuda(), compute_dtype=TORCH_DT[cdt], restart_after=restarts)
+    torch.cuda.synchronize()
+    xs = f64(x)
+    err = O.max_rel_fro_error(f64(y), O.ns(xs))
+    assert err <= TOL[cdt], err
+    # the oracle's own Gram form agrees with its NS (the pages' equivalence)
+    assert O.max_rel_fro_error(O.gram_ns(xs, restart_after=restarts), O.ns(xs)) <= 1e-10
+
+
+def test_gram_spiked_alpha4_workload_fp16():
+    M = require_gpu()
+    gr = S.WORKLOADS["c2_1024x4096_bf16"].groups[0]
+    announce("msign_gram_ns 1024x4096 spiked fp16 restart {2}")
+    x = S.group_batch(gr)
+    y = M.msign_gram_ns(x.cuda(), compute_dtype=torch.float16, restart_after=(2,))
+    torch.cuda.synchronize()
+    err = O.max_rel_fro_error(f64(y), O.ns(f64(x)))
+    assert err <= 2e-2, err
+
+
+def test_gram_bitwise_invariants():
+    M = require_gpu()
+    announce("msign_gram_ns invariants")
+    x = _input(160, 480, "f16", 11, batch=3).cuda()
+    y = M.msign_gram_ns(x)
+    y2 = M.msign_gram_ns(x)
+    y1 = M.msign_gram_ns(x[1:2].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    assert torch.equal(y[1:2], y1)
+    z = M.msign_gram_ns(torch.zeros_like(x))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z).item() == 0
