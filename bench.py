@@ -1,0 +1,237 @@
+"""Throughput of msign by Newton-Schulz on one MI355X.
+
+Default: the square 8192 x 8192 bf16 workload (iid N(0,1)), 5-step quintic NS
+with bf16 products, one msign per step.  Prints ONE JSON line with
+matrices/s, effective TFLOP/s ((20 alpha + 10) n^3 per msign) as a fraction
+of the bf16 dense MFMA peak, the roofline of the dominant kernel (timed with
+HIP events on the launch stream inside the timed region) and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--case NAME]
+                  [--no-cpu] [--all OUT.jsonl]
+
+`--case` picks another workload (see CASES); `--all` runs every case and
+writes one JSON line per case to OUT.jsonl (the default line is still
+printed).  Inputs are synthetic (seeded, see synthetic/) and already resident
+in HBM when the timed region starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "msign matrices/s and effective TFLOP/s (% bf16 MFMA peak), T=5 NS, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+HBM_GBS = 8000.0
+
+# name -> (workload, method, compute dtype, restarts)
+CASES = {
+    "c3_ns_bf16": ("c3_8192x8192_bf16", "ns", "bf16", ()),
+    "c1_ns_f32": ("c1_128x256_f32", "ns", "f32", ()),
+    "c1_ns_bf16": ("c1_128x256_f32", "ns", "bf16", ()),
+    "c2_ns_bf16": ("c2_1024x4096_bf16", "ns", "bf16", ()),
+    "c2_gram_f16": ("c2_1024x4096_bf16", "gram", "f16", (2,)),
+    "c4_ns_bf16": ("c4_block_bf16", "ns", "bf16", ()),
+    "c5_ns_bf16": ("c5_moe_f16", "ns", "bf16", ()),
+    "c5_gram_f16": ("c5_moe_f16", "gram", "f16", (2,)),
+}
+DEFAULT_CASE = "c3_ns_bf16"
+
+
+def dense_flops(n, m, steps=5):
+    """(20 alpha + 10) n^3 at T = 5: X X^T, A^2 and B X as dense GEMMs."""
+    return steps * (4.0 * m * n * n + 2.0 * n ** 3)
+
+
+def class_flops(n, m):
+    """Algorithmic flops of one launch of each kernel class on one matrix
+    ("Gram Newton-Schulz" §2.4 counts): a triangle product counts half of the
+    dense work, so X X^T is m n^2, an n x n product n^3 and B X (or Q X)
+    2 m n^2."""
+    return {"xxt": float(m) * n * n, "square": float(n) ** 3, "rect": 2.0 * m * n * n}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--case", default=DEFAULT_CASE, choices=sorted(CASES))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--all", default=None, help="run every case, one JSON line each, into this file")
+    ap.add_argument("--no-timing", action="store_true", help="no per-kernel event timing")
+    return ap.parse_args()
+
+
+def load_inputs(workload, device):
+    import synthetic as S
+    wl = S.WORKLOADS[workload]
+    xs = [S.group_batch(g, device=device) for g in wl.groups]
+    return wl, xs
+
+
+def cpu_baseline(wl, method, sample_seconds=30.0):
+    """The fp64 oracle on a bounded sample of the workload: its first matrix
+    of the largest group, running 2 of the 5 steps (or all of them when that
+    is cheap), scaled to matrices/s over the workload's mix."""
+    import numpy as np
+    import oracle as O
+    import synthetic as S
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = min(16, os.cpu_count() or 1)
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        if threadpool_info:
+            used = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+            cores = int(used[0]) if used else cores
+        per_matrix = []
+        descr = []
+        for g in wl.groups:
+            m = S.as_f64(S.group_matrix(g, 0))
+            n_, m_ = min(m.shape), max(m.shape)
+            work = dense_flops(n_, m_)
+            steps_run = 5 if work < 2e11 else 2
+            t0 = time.perf_counter()
+            if method == "ns":
+                O.ns_single(m, steps=steps_run)
+            else:
+                O.gram_ns_single(m, steps=steps_run, restart_after=(2,) if steps_run > 2 else ())
+            dt = time.perf_counter() - t0
+            per_matrix.append((g.batch, dt * 5.0 / steps_run))
+            descr.append(f"{g.rows}x{g.cols}: {steps_run} of 5 steps on matrix 0"
+                         + ("" if steps_run == 5 else ", scaled x5/2"))
+        total = sum(b * t for b, t in per_matrix)
+        nmat = sum(b for b, _ in per_matrix)
+        return {"value": nmat / total, "unit": "matrices/s", "cores": cores, "kind": "oracle",
+                "sample": "fp64 NumPy oracle (" + method + "), " + "; ".join(descr)
+                          + f"; batch mix {[b for b, _ in per_matrix]} weighted"}
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+
+
+def run_case(name, steps, warmup, with_cpu, with_timing):
+    import torch
+    import msign_newton_schulz_amd as M
+
+    workload, method, cdt, restarts = CASES[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl, xs = load_inputs(workload, dev)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cdt]
+    outs = [torch.empty_like(x) for x in xs]
+    wss = []
+    for x in xs:
+        b, r, c = x.shape
+        nb = (M.ns_workspace_bytes(b, r, c, tdt) if method == "ns"
+              else M.gram_ns_workspace_bytes(b, r, c, tdt))
+        wss.append(torch.empty(max(nb, 1), dtype=torch.uint8, device=dev))
+
+    def one_step():
+        for x, y, ws in zip(xs, outs, wss):
+            if method == "ns":
+                M.msign_ns(x, compute_dtype=tdt, out=y, workspace=ws)
+            else:
+                M.msign_gram_ns(x, compute_dtype=tdt, restart_after=restarts, out=y, workspace=ws)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    if with_timing:
+        M.kernel_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ktime = M.read_kernel_timing() if with_timing else None
+    if with_timing:
+        M.kernel_timing(False)
+
+    elapsed = t1 - t0
+    nmat = sum(x.shape[0] for x in xs)
+    eff = 0.0
+    cls_flops = {"xxt": 0.0, "square": 0.0, "rect": 0.0}
+    shapes = []
+    for x in xs:
+        b, r, c = x.shape
+        n_, m_ = min(r, c), max(r, c)
+        eff += b * dense_flops(n_, m_)
+        shapes.append([int(b), int(r), int(c)])
+        for k, v in class_flops(n_, m_).items():
+            cls_flops[k] += b * v
+    ms = 1e3 * elapsed / steps
+    eff_tflops = eff * steps / elapsed / 1e12
+    rec = {
+        "metric": METRIC, "value": nmat * steps / elapsed, "unit": "matrices/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cdt, "data": "synthetic",
+        "config": {"workload": workload, "case": name, "method": "msign_" + ("ns" if method == "ns" else "gram_ns"),
+                   "shapes": shapes, "T": 5, "compute": cdt, "restart_after": list(restarts),
+                   "parallelism": "single GPU"},
+        "effective_tflops": eff_tflops,
+        "effective_frac_of_peak": eff_tflops / PEAK_TFLOPS[cdt],
+    }
+    if ktime is not None:
+        per = {}
+        for k in ("normalize", "xxt", "square", "rect"):
+            tot, cnt = ktime[k]
+            per[k] = {"total_ms": tot, "launches": cnt, "avg_us": 1e3 * tot / cnt if cnt else None}
+        rec["kernels"] = per
+        dom = max(("xxt", "square", "rect"), key=lambda k: ktime[k][0])
+        tot, cnt = ktime[dom]
+        if cnt:
+            # every group's call makes the same number of launches of a class;
+            # one launch processes that group's whole batch
+            groups = len(xs)
+            flops_per_launch = cls_flops[dom] / groups
+            avg_s = tot / cnt / 1e3
+            ach = flops_per_launch / avg_s / 1e12
+            rec["roofline"] = {"bound": "mfma", "kernel": f"gemm_nt_kernel ({dom})", "achieved": ach,
+                               "peak": PEAK_TFLOPS[cdt], "unit": "TFLOP/s",
+                               "frac": ach / PEAK_TFLOPS[cdt], "traffic": None,
+                               "avg_launch_us": avg_s * 1e6,
+                               "algorithmic_flops_per_launch": flops_per_launch}
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(wl, method)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(msign shards by batch across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.all:
+        with open(args.all, "w") as f:
+            for name in CASES:
+                print(f"[bench] case {name}", file=sys.stderr, flush=True)
+                steps = args.steps if not name.startswith("c4") else max(3, args.steps // 4)
+                rec = run_case(name, steps, args.warmup, with_cpu=False, with_timing=not args.no_timing)
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                print(f"[bench] {name}: {rec['value']:.4g} matrices/s, "
+                      f"{rec['effective_tflops']:.1f} effective TFLOP/s", file=sys.stderr, flush=True)
+    rec = run_case(args.case, args.steps, args.warmup, with_cpu=not args.no_cpu,
+                   with_timing=not args.no_timing)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,7 +150,8 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch,
  *          D must be symmetric; its upper triangle is what is read.
  *   workspace, workspace_bytes  device scratch of at least
  *          syrk_xxt_workspace_bytes(...) bytes (0 bytes, NULL allowed, when
- *          k is a multiple of 8 elements for bf16/f16 and of 4 for f32).
+ *          k is a multiple of 64 and x is 16-byte aligned; otherwise x is
+ *          first copied into a zero-padded buffer there).
  */
 size_t syrk_xxt_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t dtype);
 

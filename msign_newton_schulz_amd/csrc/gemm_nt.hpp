@@ -34,6 +34,8 @@
 
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace msign {
 
 #define MSIGN_MAX_OUT 3
@@ -54,7 +56,7 @@ struct OutSpec {
 struct GemmParams {
   const void* P; int64_t ldp, sp;
   const void* Q; int64_t ldq, sq;
-  int32_t M, N, K;     // load bounds; K a multiple of 16 bytes of elements
+  int32_t M, N, K;     // load bounds; K a multiple of 64 elements
   float alpha, beta;
   const void* Dt; int64_t ldd, sd; int32_t d_dtype; int32_t d_vec_ok;
   OutSpec out[MSIGN_MAX_OUT];
@@ -76,11 +78,12 @@ template <> struct Mma<f16_t> {
   }
 };
 template <> struct Mma<float> {
+  // Bit-cast the whole fragment first: a bit_cast of one vector element
+  // does not select that element.
   static __device__ __forceinline__ void run(f32x4& acc, const u32x4& a, const u32x4& b) {
+    const f32x4 fa = __builtin_bit_cast(f32x4, a), fb = __builtin_bit_cast(f32x4, b);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[e]),
-                                                 __builtin_bit_cast(float, b[e]), acc, 0, 0, 0);
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], fb[e], acc, 0, 0, 0);
   }
 };
 
@@ -120,20 +123,41 @@ __device__ __forceinline__ void load_vec4(const void* ptr, int64_t base, int32_t
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool TRI>
+// 16-byte chunk position inside an LDS row of CPR chunks: XOR swizzle so
+// that the 16 lanes reading one fragment column (16 consecutive rows, same
+// logical chunk) hit distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int ch) {
+  if constexpr (CPR == 8) return ch ^ (row & 7);
+  else return ch ^ ((row >> 1) & 3);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2; renumber so that every XCD works on one contiguous range of tiles.
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7, x = b & 7, l = b >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + l;
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_kernel(const GemmParams p) {
   constexpr int NT = WGM * WGN * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int ESZ = Elem<T>::size;
-  constexpr int CE = 16 / ESZ;   // elements per 16-byte chunk
-  constexpr int KTE = 8 * CE;    // elements per 128-byte K slice
-  constexpr int ACH = BM * 8 / NT, BCH = BN * 8 / NT;
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile/thread mismatch");
+  constexpr int CE = 16 / ESZ;      // elements per 16-byte chunk
+  constexpr int CPR = BKB / 16;     // chunks per row of one K slice
+  constexpr int KTE = CPR * CE;     // elements per K slice
+  constexpr int KSUB = CPR / 4;     // MFMA K sub-steps per slice (4 lane groups)
+  constexpr int ACH = BM * CPR / NT, BCH = BN * CPR / NT;
+  constexpr int GM = 8;             // tile rows per group of the grouped order
+  static_assert(CPR == 4 || CPR == 8, "K slice must be 64 or 128 bytes");
+  static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile/thread mismatch");
   static_assert(!TRI || BM == BN, "triangle mode needs square tiles");
+  static_assert(NST >= 1 && NST <= 3, "one to three K slices of register prefetch");
 
-  __shared__ u32x4 lds[2][(BM + BN) * 8];
+  __shared__ u32x4 lds[2][(BM + BN) * CPR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,53 +165,74 @@ gemm_nt_kernel(const GemmParams p) {
   const int wm = wave / WGN, wn = wave % WGN;
   const int64_t bz = blockIdx.z;
 
+  // ---- tile of this block ----
+  const int idx = xcd_contiguous(blockIdx.x, gridDim.x);
   int ti, tj;
   if constexpr (TRI) {
-    int t = blockIdx.x, r = 0, rowlen = p.tiles_n;
-    while (t >= rowlen) { t -= rowlen; ++r; --rowlen; }
-    ti = r;
-    tj = r + t;
+    // Fold the upper triangle of a Tv x Tv grid (Tv even) into a Tv/2 x (Tv+1)
+    // rectangle: folded row f holds tile row f (Tv - f tiles) followed by tile
+    // row Tv-1-f (f + 1 tiles).  A virtual last row/column pads odd T.
+    const int TT = p.tiles_n, Tv = TT + (TT & 1), H = Tv / 2, W = Tv + 1;
+    const int per = GM * W, g = idx / per, first = g * GM;
+    const int gm = H - first < GM ? H - first : GM;
+    const int rr = idx - g * per;
+    const int f = first + rr % gm, c = rr / gm;
+    if (c < Tv - f) { ti = f; tj = f + c; }
+    else { ti = Tv - 1 - f; tj = ti + (c - (Tv - f)); }
+    if (tj >= TT) return;  // virtual tile (whole block leaves before any barrier)
   } else {
-    ti = blockIdx.x % p.tiles_m;
-    tj = blockIdx.x / p.tiles_m;
+    const int tm = p.tiles_m;
+    const int per = GM * p.tiles_n, g = idx / per, first = g * GM;
+    const int gm = tm - first < GM ? tm - first : GM;
+    const int rr = idx - g * per;
+    ti = first + rr % gm;
+    tj = rr / gm;
   }
   const int m0 = ti * BM, n0 = tj * BN;
 
-  const char* Pb = static_cast<const char*>(p.P) + bz * p.sp * ESZ;
-  const char* Qb = static_cast<const char*>(p.Q) + bz * p.sq * ESZ;
+  // Buffer descriptors start at this tile's first row; rows past M (or N)
+  // fall outside num_records, so those loads return zeros without branches.
+  const char* Pt = static_cast<const char*>(p.P) + (bz * p.sp + (int64_t)m0 * p.ldp) * ESZ;
+  const char* Qt = static_cast<const char*>(p.Q) + (bz * p.sq + (int64_t)n0 * p.ldq) * ESZ;
+  const int prow = p.M - m0 < BM ? p.M - m0 : BM;
+  const int qrow = p.N - n0 < BN ? p.N - n0 : BN;
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Pt, (short)0, prow > 0 ? (int)((int64_t)prow * p.ldp * ESZ) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Qt, (short)0, qrow > 0 ? (int)((int64_t)qrow * p.ldq * ESZ) : 0, 0x00020000);
 
-  u32x4 ra[ACH], rb[BCH];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  // Each thread moves chunks (row0 + s * RSTEP, ch) for s < ACH (and BCH):
+  // the same K column and swizzle for every s, since RSTEP is a multiple of
+  // the swizzle period.
+  constexpr int RSTEP = NT / CPR;
+  static_assert(RSTEP % 8 == 0, "row step must keep the swizzle");
+  const int row0 = tid / CPR, ch0 = tid % CPR;
+  const int kcol = ch0 * CE;
+  const int a_base = (row0 * (int)p.ldp + kcol) * ESZ;
+  const int b_base = (row0 * (int)p.ldq + kcol) * ESZ;
+  const int a_step = RSTEP * (int)p.ldp * ESZ;
+  const int b_step = RSTEP * (int)p.ldq * ESZ;
+  const int lds_w = row0 * CPR + swz<CPR>(row0, ch0);  // + s * RSTEP * CPR
 
-  auto gload = [&](int k0) {
+
+  // K is a multiple of 64 elements (host contract), so every slice is whole;
+  // slices past the end (the last prefetches) read past the row or past
+  // num_records and are never copied into LDS.
+  auto gload = [&](u32x4* dst, int k0) {
 #pragma unroll
-    for (int s = 0; s < ACH; ++s) {
-      const int cid = tid + s * NT, row = cid >> 3, ch = cid & 7;
-      const int gr = m0 + row, kk = k0 + ch * CE;
-      ra[s] = (gr < p.M && kk < p.K)
-                  ? *reinterpret_cast<const u32x4*>(Pb + ((int64_t)gr * p.ldp + kk) * ESZ)
-                  : zero4;
-    }
+    for (int s = 0; s < ACH; ++s)
+      dst[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, a_base + s * a_step + k0 * ESZ, 0, 0));
 #pragma unroll
-    for (int s = 0; s < BCH; ++s) {
-      const int cid = tid + s * NT, row = cid >> 3, ch = cid & 7;
-      const int gr = n0 + row, kk = k0 + ch * CE;
-      rb[s] = (gr < p.N && kk < p.K)
-                  ? *reinterpret_cast<const u32x4*>(Qb + ((int64_t)gr * p.ldq + kk) * ESZ)
-                  : zero4;
-    }
+    for (int s = 0; s < BCH; ++s)
+      dst[ACH + s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, b_base + s * b_step + k0 * ESZ, 0, 0));
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const u32x4* src, int buf) {
 #pragma unroll
-    for (int s = 0; s < ACH; ++s) {
-      const int cid = tid + s * NT, row = cid >> 3, ch = cid & 7;
-      lds[buf][row * 8 + (ch ^ (row & 7))] = ra[s];
-    }
+    for (int s = 0; s < ACH; ++s) lds[buf][lds_w + s * RSTEP * CPR] = src[s];
 #pragma unroll
-    for (int s = 0; s < BCH; ++s) {
-      const int cid = tid + s * NT, row = cid >> 3, ch = cid & 7;
-      lds[buf][(BM + row) * 8 + (ch ^ (row & 7))] = rb[s];
-    }
+    for (int s = 0; s < BCH; ++s) lds[buf][BM * CPR + lds_w + s * RSTEP * CPR] = src[ACH + s];
   };
 
   f32x4 acc[FM][FN];
@@ -196,41 +241,85 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = (p.K + KTE - 1) / KTE;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * KTE);
+  // Small wave tiles read all A and B fragments of a sub-step before its
+  // MFMAs (the reads overlap each other and the first products); the
+  // 128 x 128 wave tile holds its A fragments and streams B fragments one at
+  // a time to stay within the register file next to 256 accumulators.
+  constexpr bool kAllFrags = (FM + FN) <= 12;
+  auto compute = [&](int buf) {
+    __builtin_amdgcn_s_setprio(1);  // favour waves that are issuing MFMAs
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KSUB; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
-      u32x4 a[FM], b[FN];
+      u32x4 a[FM];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int row = wm * WM + fm * 16 + (lane & 15);
-        a[fm] = lds[buf][row * 8 + (ch ^ (row & 7))];
+        a[fm] = lds[buf][row * CPR + swz<CPR>(row, ch)];
       }
+      if constexpr (kAllFrags) {
+        u32x4 b[FN];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int row = wn * WN + fn * 16 + (lane & 15);
-        b[fn] = lds[buf][(BM + row) * 8 + (ch ^ (row & 7))];
+        for (int fn = 0; fn < FN; ++fn) {
+          const int row = wn * WN + fn * 16 + (lane & 15);
+          b[fn] = lds[buf][(BM + row) * CPR + swz<CPR>(row, ch)];
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) Mma<T>::run(acc[fm][fn], a[fm], b[fn]);
+      } else {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int row = wn * WN + fn * 16 + (lane & 15);
+          const u32x4 b = lds[buf][(BM + row) * CPR + swz<CPR>(row, ch)];
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) Mma<T>::run(acc[fm][fn], a[fm], b);
+        }
       }
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) Mma<T>::run(acc[fm][fn], a[fm], b[fn]);
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Register prefetch of NST K slices: slice t lives in stg[t % NST] from
+  // its load (issued NST iterations ahead) until it is copied into LDS
+  // buffer t % 2 one iteration before its use.  Prefetches are issued
+  // unconditionally (past the end of K they read nothing that is used), so
+  // the wait before an LDS copy covers only the oldest slice and leaves the
+  // newer ones in flight.
+  const int KT = (p.K + KTE - 1) / KTE;
+  u32x4 stg[NST][ACH + BCH];
+  gload(stg[0], 0);
+  if constexpr (NST >= 2) gload(stg[1], KTE);
+  if constexpr (NST >= 3) gload(stg[2], 2 * KTE);
+  if (KT > 0) lstore(stg[0], 0);
+  __syncthreads();
+  auto iter = [&](int kt, auto S) {
+    constexpr int s = decltype(S)::value;  // kt % NST
+    gload(stg[s], (kt + NST) * KTE);
+    compute(kt & 1);
+    if (kt + 1 < KT) lstore(stg[(s + 1) % NST], (kt + 1) & 1);
     __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, (1 % NST)>;
+  using I2 = std::integral_constant<int, (2 % NST)>;
+  int kt = 0;
+  for (; kt + NST <= KT; kt += NST) {
+    iter(kt, I0{});
+    if constexpr (NST >= 2) iter(kt + 1, I1{});
+    if constexpr (NST >= 3) iter(kt + 2, I2{});
+  }
+  if (kt < KT) iter(kt, I0{});
+  if constexpr (NST >= 3) {
+    if (kt + 1 < KT) iter(kt + 1, I1{});
   }
 
   // ---- epilogue ----
   const bool diag_tile = TRI && (ti == tj);
-#pragma unroll
+#pragma clang loop unroll(full)
   for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int fn = 0; fn < FN; ++fn) {
       const int i0 = m0 + wm * WM + fm * 16 + 4 * (lane >> 4);
       const int j = n0 + wn * WN + fn * 16 + (lane & 15);

@@ -48,7 +48,7 @@ msign_status_t fail(msign_status_t st, const std::string& msg) {
 constexpr float kKeller[3] = {3.4445f, -4.7750f, 2.0315f};
 
 constexpr int64_t kPad = 64;
-constexpr int64_t kMaxDim = int64_t(1) << 21;
+constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxBatch = 65535;
 
 int64_t pad_up(int64_t v) { return (v + kPad - 1) / kPad * kPad; }
@@ -197,16 +197,36 @@ enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3 };
 
 // --------------------------------------------------------------- launches --
 
-constexpr int kBM = 128, kBN = 128;
+// Tile configurations (measured on MI355X, 8192^2 bf16): 256 x 256 tiles
+// with 16 waves of 64 x 64 (4 waves per SIMD hide LDS and MFMA latency; the
+// 64 accumulators per lane stay in VGPRs) when the problem has at least one
+// full round of such tiles for the 256 CUs; otherwise 128 x 128 tiles with
+// 4 waves of 64 x 64.  K slices are 64 bytes with two slices of register
+// prefetch.
+constexpr int kCUs = 256;
+
+int tri_blocks(int tiles) {
+  const int tv = tiles + (tiles & 1);
+  return tv / 2 * (tv + 1);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
+hipError_t launch_cfg(GemmParams q, int64_t batch, hipStream_t st) {
+  q.tiles_m = (q.M + BM - 1) / BM;
+  q.tiles_n = (q.N + BN - 1) / BN;
+  const unsigned gx = TRI ? (unsigned)tri_blocks(q.tiles_m) : (unsigned)(q.tiles_m * q.tiles_n);
+  if (gx == 0) return hipSuccess;
+  dim3 grid(gx, 1, (unsigned)batch);
+  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI><<<grid, WGM * WGN * 64, 0, st>>>(q);
+  return hipGetLastError();
+}
 
 template <typename T, bool TRI>
-hipError_t launch_nt_t(GemmParams q, int64_t batch, hipStream_t st) {
-  q.tiles_m = (q.M + kBM - 1) / kBM;
-  q.tiles_n = (q.N + kBN - 1) / kBN;
-  const unsigned gx = TRI ? (unsigned)(q.tiles_m * (q.tiles_m + 1) / 2) : (unsigned)(q.tiles_m * q.tiles_n);
-  dim3 grid(gx, 1, (unsigned)batch);
-  gemm_nt_kernel<T, kBM, kBN, 2, 2, TRI><<<grid, 256, 0, st>>>(q);
-  return hipGetLastError();
+hipError_t launch_nt_t(const GemmParams& q, int64_t batch, hipStream_t st) {
+  const int64_t t256 = (int64_t)((q.M + 255) / 256) * ((q.N + 255) / 256);
+  const int64_t tiles = (TRI ? (t256 + (q.M + 255) / 256) / 2 : t256) * batch;
+  if (tiles >= kCUs) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI>(q, batch, st);
+  return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI>(q, batch, st);
 }
 
 hipError_t launch_nt(int32_t cdt, bool tri, const GemmParams& q, int64_t batch, hipStream_t st) {
@@ -266,7 +286,7 @@ msign_status_t check_common(const void* x, void* y, int64_t batch, int64_t rows,
   if (!dt_valid(compute_dtype)) return fail(MSIGN_ERR_DTYPE, "compute_dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
   if (batch < 0 || rows < 0 || cols < 0) return fail(MSIGN_ERR_SHAPE, "batch, rows and cols must be >= 0");
   if (batch > kMaxBatch) return fail(MSIGN_ERR_SHAPE, "batch must be <= 65535");
-  if (rows > kMaxDim || cols > kMaxDim) return fail(MSIGN_ERR_SHAPE, "rows and cols must be <= 2^21");
+  if (rows > kMaxDim || cols > kMaxDim) return fail(MSIGN_ERR_SHAPE, "rows and cols must be <= 2^20");
   if (steps < 1 || steps > MSIGN_MAX_STEPS) return fail(MSIGN_ERR_ARG, "steps must be in 1..64");
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MSIGN_ERR_ARG, "eps must be finite and >= 0");
   if (coeffs) {
@@ -548,8 +568,7 @@ size_t syrk_xxt_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t dty
   if (batch < 0 || n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || batch > kMaxBatch || !dt_valid(dtype))
     return (size_t)-1;
   if (batch == 0 || n == 0 || k == 0) return 0;
-  const int64_t ce = 16 / (int64_t)dt_size(dtype);
-  if (k % ce == 0) return 0;
+  if (k % kPad == 0) return 0;
   return align256((size_t)batch * pad_up(n) * pad_up(k) * dt_size(dtype));
 }
 
@@ -560,7 +579,7 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_
   if (!dt_valid(dtype)) return fail(MSIGN_ERR_DTYPE, "dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
   if (batch < 0 || n < 0 || k < 0) return fail(MSIGN_ERR_SHAPE, "batch, n and k must be >= 0");
   if (batch > kMaxBatch) return fail(MSIGN_ERR_SHAPE, "batch must be <= 65535");
-  if (n > kMaxDim || k > kMaxDim) return fail(MSIGN_ERR_SHAPE, "n and k must be <= 2^21");
+  if (n > kMaxDim || k > kMaxDim) return fail(MSIGN_ERR_SHAPE, "n and k must be <= 2^20");
   if (!std::isfinite(alpha) || !std::isfinite(beta) || !std::isfinite(gamma))
     return fail(MSIGN_ERR_ARG, "alpha, beta and gamma must be finite");
   if (batch == 0 || n == 0) return MSIGN_OK;
@@ -574,8 +593,9 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_
     return fail(MSIGN_ERR_ALIAS, "c overlaps x");
   if (d && overlap(d, c_bytes, c, c_bytes)) return fail(MSIGN_ERR_ALIAS, "c overlaps d");
   const size_t need = syrk_xxt_workspace_bytes(batch, n, k, dtype);
-  const int64_t ce = 16 / (int64_t)es;
-  const bool direct = (k % ce == 0) && aligned(x, 16);
+  // the product kernel reads K in whole 64-element slices from 16-byte
+  // aligned rows; other inputs are first copied into a padded buffer
+  const bool direct = (k % kPad == 0) && aligned(x, 16);
   if (!direct && k > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(MSIGN_ERR_WORKSPACE, "workspace is null or smaller than the required " + std::to_string(need) + " bytes");

@@ -88,7 +88,7 @@ def test_ns_argument_errors_before_launch():
     assert _ns(lib, cdt=-1) == 2
     assert _ns(lib, rows=-1) == 3
     assert _ns(lib, batch=70000) == 3
-    assert _ns(lib, cols=1 << 22) == 3
+    assert _ns(lib, cols=(1 << 20) + 1) == 3
     assert _ns(lib, steps=0) == 1
     assert _ns(lib, steps=65) == 1
     assert _ns(lib, eps=-1.0) == 1
@@ -137,6 +137,7 @@ def test_syrk_argument_errors():
     assert f(FAKE, FAKE, 1, 8, 16, 1, 1.0, None, 0.0, 0.0, None, 0, None) == 5
     # ragged k needs a workspace
     assert f(FAKE, FAKE2, 1, 8, 15, 1, 1.0, None, 0.0, 0.0, None, 0, None) == 4
+    assert f(FAKE, FAKE2, 1, 8, 16, 1, 1.0, None, 0.0, 0.0, None, 0, None) == 4
     assert f(FAKE, FAKE2, 0, 8, 16, 1, 1.0, None, 0.0, 0.0, None, 0, None) == 0
 
 
