@@ -69,7 +69,24 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", default=None, help="run every case, one JSON line each, into this file")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel event timing")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of msign, run 3 plain device copies of this many bytes "
+                         "(calibrates the HBM traffic counters)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes):
+    """Three device-to-device copies of `nbytes` with torch's copy kernel; the
+    FETCH_SIZE/WRITE_SIZE counters of these dispatches give the scale of the
+    counters against a known byte count."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def load_inputs(workload, device):
@@ -213,6 +230,9 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
 
 def main():
     args = parse()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               "(msign shards by batch across GPUs with no exchange; see the design notes)",

@@ -148,10 +148,12 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch,
  *          store) or MSIGN_F32.
  *   d      device, [batch, n, n] in dtype, or NULL (then beta is ignored).
  *          D must be symmetric; its upper triangle is what is read.
- *   workspace, workspace_bytes  device scratch of at least
- *          syrk_xxt_workspace_bytes(...) bytes (0 bytes, NULL allowed, when
- *          k is a multiple of 64 and x is 16-byte aligned; otherwise x is
- *          first copied into a zero-padded buffer there).
+ *   workspace, workspace_bytes  device scratch, 256-byte aligned.
+ *          syrk_xxt_workspace_bytes() is the size for the fastest path: a
+ *          zero-padded copy of x (needed only when k is not a multiple of 64
+ *          or x is not 16-byte aligned; then it is required) followed by
+ *          scratch for splitting the last round of tiles along K (optional:
+ *          with less, or NULL, those tiles are computed whole).
  */
 size_t syrk_xxt_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t dtype);
 

@@ -62,6 +62,12 @@ struct GemmParams {
   OutSpec out[MSIGN_MAX_OUT];
   int32_t nout;
   int32_t tiles_m, tiles_n;
+  // Blocks enumerate tiles over the whole batch (tpm tiles per matrix).  The
+  // first nfull tiles are computed whole; each later tile is split along K
+  // into `split` parts whose fp32 sums go to `partial` and are added in a
+  // fixed order by gemm_nt_reduce_kernel.
+  int32_t tpm, nfull, split;
+  float* partial;
 };
 
 template <typename T> struct Mma;
@@ -139,6 +145,107 @@ __device__ __forceinline__ int xcd_contiguous(int b, int nb) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + l;
 }
 
+// Tile coordinates of linear tile L over the batch: matrix bz, tile
+// (ti, tj).  Rectangular grids are walked in groups of GM tile rows, column
+// by column, so that concurrently running tiles share operand strips in L2.
+// The upper triangle of a Tv x Tv grid (Tv = T rounded up to even) is folded
+// into a Tv/2 x (Tv+1) rectangle: folded row f holds tile row f (Tv - f
+// tiles) followed by tile row Tv-1-f (f + 1 tiles).  Returns false for the
+// virtual tiles that pad an odd T.
+template <bool TRI>
+__device__ __forceinline__ bool tile_of(const GemmParams& p, int L, int64_t& bz, int& ti, int& tj) {
+  constexpr int GM = 8;
+  bz = L / p.tpm;
+  const int idx = L - (int)bz * p.tpm;
+  if constexpr (TRI) {
+    const int TT = p.tiles_n, Tv = TT + (TT & 1), H = Tv / 2, W = Tv + 1;
+    const int per = GM * W, g = idx / per, first = g * GM;
+    const int gm = H - first < GM ? H - first : GM;
+    const int rr = idx - g * per;
+    const int f = first + rr % gm, c = rr / gm;
+    if (c < Tv - f) { ti = f; tj = f + c; }
+    else { ti = Tv - 1 - f; tj = ti + (c - (Tv - f)); }
+    return tj < TT;
+  } else {
+    const int tm = p.tiles_m;
+    const int per = GM * p.tiles_n, g = idx / per, first = g * GM;
+    const int gm = tm - first < GM ? tm - first : GM;
+    const int rr = idx - g * per;
+    ti = first + rr % gm;
+    tj = rr / gm;
+    return true;
+  }
+}
+
+// Epilogue on the fp32 accumulators of one tile (lane layout of the 16x16
+// MFMA): alpha*acc + beta*D (D read through its transpose Dt[j][i], four
+// consecutive values per lane), a per-output diagonal term, then each
+// output's stores.  Triangle mode stores the tile and its mirror; in a
+// diagonal tile only i <= j is kept.
+template <int BM, int BN, int WGM, int WGN, bool TRI>
+__device__ __forceinline__ void epilogue(const GemmParams& p, int64_t bz, int ti, int tj,
+                                         const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16]) {
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int m0 = ti * BM, n0 = tj * BN;
+  const bool diag_tile = TRI && (ti == tj);
+#pragma clang loop unroll(full)
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma clang loop unroll(full)
+    for (int fn = 0; fn < FN; ++fn) {
+      const int i0 = m0 + wm * WM + fm * 16 + 4 * (lane >> 4);
+      const int j = n0 + wn * WN + fn * 16 + (lane & 15);
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[fm][fn][r];
+      if (p.Dt != nullptr && j < p.N && i0 < p.M) {
+        float d[4];
+        const int64_t base = bz * p.sd + (int64_t)j * p.ldd + i0;
+        if (p.d_vec_ok && i0 + 3 < p.M) {
+          load_vec4(p.Dt, base, p.d_dtype, d);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d[r] = (i0 + r < p.M) ? load_as_f32(p.Dt, base + r, p.d_dtype) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += p.beta * d[r];
+      }
+      for (int o = 0; o < p.nout; ++o) {
+        const OutSpec& os = p.out[o];
+        float w[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = i0 + r;
+          w[r] = v[r] + ((i == j && i < os.diag_lim) ? os.diag : 0.f);
+        }
+        if (j >= os.cols_lim) continue;
+        if (TRI || !os.transposed) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = i0 + r;
+            if (i < os.rows_lim && (!diag_tile || i <= j)) store_elem(os, bz, i, j, w[r]);
+          }
+        }
+        if (TRI || os.transposed) {
+          // element (i, j) goes to ptr[j * ld + i]; in triangle mode this is the mirror
+          const int64_t base = bz * os.bstride + (int64_t)j * os.ld + i0;
+          if (os.vec_ok && !diag_tile && i0 + 3 < os.rows_lim) {
+            store_vec4(os.ptr, base, os.dtype, w);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = i0 + r;
+              if (i < os.rows_lim && (!diag_tile || i < j)) store_from_f32(os.ptr, base + r, os.dtype, w[r]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 gemm_nt_kernel(const GemmParams p) {
@@ -151,7 +258,6 @@ gemm_nt_kernel(const GemmParams p) {
   constexpr int KTE = CPR * CE;     // elements per K slice
   constexpr int KSUB = CPR / 4;     // MFMA K sub-steps per slice (4 lane groups)
   constexpr int ACH = BM * CPR / NT, BCH = BN * CPR / NT;
-  constexpr int GM = 8;             // tile rows per group of the grouped order
   static_assert(CPR == 4 || CPR == 8, "K slice must be 64 or 128 bytes");
   static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile/thread mismatch");
   static_assert(!TRI || BM == BN, "triangle mode needs square tiles");
@@ -163,31 +269,22 @@ gemm_nt_kernel(const GemmParams p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int64_t bz = blockIdx.z;
 
-  // ---- tile of this block ----
-  const int idx = xcd_contiguous(blockIdx.x, gridDim.x);
-  int ti, tj;
-  if constexpr (TRI) {
-    // Fold the upper triangle of a Tv x Tv grid (Tv even) into a Tv/2 x (Tv+1)
-    // rectangle: folded row f holds tile row f (Tv - f tiles) followed by tile
-    // row Tv-1-f (f + 1 tiles).  A virtual last row/column pads odd T.
-    const int TT = p.tiles_n, Tv = TT + (TT & 1), H = Tv / 2, W = Tv + 1;
-    const int per = GM * W, g = idx / per, first = g * GM;
-    const int gm = H - first < GM ? H - first : GM;
-    const int rr = idx - g * per;
-    const int f = first + rr % gm, c = rr / gm;
-    if (c < Tv - f) { ti = f; tj = f + c; }
-    else { ti = Tv - 1 - f; tj = ti + (c - (Tv - f)); }
-    if (tj >= TT) return;  // virtual tile (whole block leaves before any barrier)
+  // ---- tile (or K part of a tile) of this block ----
+  // Whole tiles come first in block order, renumbered XCD-contiguously among
+  // themselves; the K parts of the split tiles follow, dealt round-robin.
+  const int b = blockIdx.x;
+  int L, part = -1, unit = 0;
+  if (b < p.nfull) {
+    L = xcd_contiguous(b, p.nfull);
   } else {
-    const int tm = p.tiles_m;
-    const int per = GM * p.tiles_n, g = idx / per, first = g * GM;
-    const int gm = tm - first < GM ? tm - first : GM;
-    const int rr = idx - g * per;
-    ti = first + rr % gm;
-    tj = rr / gm;
+    unit = b - p.nfull;
+    L = p.nfull + unit / p.split;
+    part = unit % p.split;
   }
+  int64_t bz;
+  int ti, tj;
+  if (!tile_of<TRI>(p, L, bz, ti, tj)) return;  // whole block, before any barrier
   const int m0 = ti * BM, n0 = tj * BN;
 
   // Buffer descriptors start at this tile's first row; rows past M (or N)
@@ -288,88 +385,76 @@ gemm_nt_kernel(const GemmParams p) {
   // the wait before an LDS copy covers only the oldest slice and leaves the
   // newer ones in flight.
   const int KT = (p.K + KTE - 1) / KTE;
+  int kt0 = 0, nk = KT;
+  if (part >= 0) {
+    kt0 = (int)((int64_t)part * KT / p.split);
+    nk = (int)((int64_t)(part + 1) * KT / p.split) - kt0;
+  }
   u32x4 stg[NST][ACH + BCH];
-  gload(stg[0], 0);
-  if constexpr (NST >= 2) gload(stg[1], KTE);
-  if constexpr (NST >= 3) gload(stg[2], 2 * KTE);
-  if (KT > 0) lstore(stg[0], 0);
+  gload(stg[0], kt0 * KTE);
+  if constexpr (NST >= 2) gload(stg[1], (kt0 + 1) * KTE);
+  if constexpr (NST >= 3) gload(stg[2], (kt0 + 2) * KTE);
+  if (nk > 0) lstore(stg[0], 0);
   __syncthreads();
-  auto iter = [&](int kt, auto S) {
-    constexpr int s = decltype(S)::value;  // kt % NST
-    gload(stg[s], (kt + NST) * KTE);
-    compute(kt & 1);
-    if (kt + 1 < KT) lstore(stg[(s + 1) % NST], (kt + 1) & 1);
+  auto iter = [&](int j, auto S) {
+    constexpr int s = decltype(S)::value;  // j % NST
+    gload(stg[s], (kt0 + j + NST) * KTE);
+    compute(j & 1);
+    if (j + 1 < nk) lstore(stg[(s + 1) % NST], (j + 1) & 1);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, (1 % NST)>;
   using I2 = std::integral_constant<int, (2 % NST)>;
-  int kt = 0;
-  for (; kt + NST <= KT; kt += NST) {
-    iter(kt, I0{});
-    if constexpr (NST >= 2) iter(kt + 1, I1{});
-    if constexpr (NST >= 3) iter(kt + 2, I2{});
+  int j = 0;
+  for (; j + NST <= nk; j += NST) {
+    iter(j, I0{});
+    if constexpr (NST >= 2) iter(j + 1, I1{});
+    if constexpr (NST >= 3) iter(j + 2, I2{});
   }
-  if (kt < KT) iter(kt, I0{});
+  if (j < nk) iter(j, I0{});
   if constexpr (NST >= 3) {
-    if (kt + 1 < KT) iter(kt + 1, I1{});
+    if (j + 1 < nk) iter(j + 1, I1{});
   }
 
-  // ---- epilogue ----
-  const bool diag_tile = TRI && (ti == tj);
-#pragma clang loop unroll(full)
-  for (int fm = 0; fm < FM; ++fm) {
-#pragma clang loop unroll(full)
-    for (int fn = 0; fn < FN; ++fn) {
-      const int i0 = m0 + wm * WM + fm * 16 + 4 * (lane >> 4);
-      const int j = n0 + wn * WN + fn * 16 + (lane & 15);
-      float v[4];
+  if (part >= 0) {  // partial sums of this K range, one f32x4 per thread and fragment
+    f32x4* dst = reinterpret_cast<f32x4*>(p.partial) + (int64_t)unit * (FM * FN * NT);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[fm][fn][r];
-      if (p.Dt != nullptr && j < p.N && i0 < p.M) {
-        float d[4];
-        const int64_t base = bz * p.sd + (int64_t)j * p.ldd + i0;
-        if (p.d_vec_ok && i0 + 3 < p.M) {
-          load_vec4(p.Dt, base, p.d_dtype, d);
-        } else {
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) d[r] = (i0 + r < p.M) ? load_as_f32(p.Dt, base + r, p.d_dtype) : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += p.beta * d[r];
-      }
-      for (int o = 0; o < p.nout; ++o) {
-        const OutSpec& os = p.out[o];
-        float w[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = i0 + r;
-          w[r] = v[r] + ((i == j && i < os.diag_lim) ? os.diag : 0.f);
-        }
-        if (j >= os.cols_lim) continue;
-        if (TRI || !os.transposed) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = i0 + r;
-            if (i < os.rows_lim && (!diag_tile || i <= j)) store_elem(os, bz, i, j, w[r]);
-          }
-        }
-        if (TRI || os.transposed) {
-          // element (i, j) goes to ptr[j * ld + i]; in triangle mode this is the mirror
-          const int64_t base = bz * os.bstride + (int64_t)j * os.ld + i0;
-          if (os.vec_ok && !diag_tile && i0 + 3 < os.rows_lim) {
-            store_vec4(os.ptr, base, os.dtype, w);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = i0 + r;
-              if (i < os.rows_lim && (!diag_tile || i < j)) store_from_f32(os.ptr, base + r, os.dtype, w[r]);
-            }
-          }
-        }
-      }
-    }
+      for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * NT + tid] = acc[fm][fn];
+    return;
   }
+  epilogue<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, acc);
+}
+
+// Second pass for split tiles: one block per tile adds its parts' partial
+// sums in part order (fixed, so the result is bit-stable) and runs the same
+// epilogue as a whole tile.
+template <typename T, int BM, int BN, int WGM, int WGN, bool TRI>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+gemm_nt_reduce_kernel(const GemmParams p) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
+  const int t = blockIdx.x;
+  int64_t bz;
+  int ti, tj;
+  if (!tile_of<TRI>(p, p.nfull + t, bz, ti, tj)) return;
+  const int tid = threadIdx.x;
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.partial) + (int64_t)t * p.split * (FM * FN * NT);
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = src[(fm * FN + fn) * NT + tid];
+  for (int sp = 1; sp < p.split; ++sp) {
+    const f32x4* s2 = src + (int64_t)sp * (FM * FN * NT);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] += s2[(fm * FN + fn) * NT + tid];
+  }
+  epilogue<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, acc);
 }
 
 }  // namespace msign

@@ -71,6 +71,9 @@ Shape canon(int64_t rows, int64_t cols) {
   return s;
 }
 
+// K-split scratch of the products of one NS or Gram call (defined below).
+size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt);
+
 int32_t norm_blocks(int64_t count) {
   int64_t nb = (count + 16383) / 16384;
   if (nb < 1) nb = 1;
@@ -90,7 +93,7 @@ struct Carver {
 struct NsPlan {
   Shape s;
   int32_t nblk;
-  size_t x32t[2], xh[2], xht[2], a, b, partial, total;
+  size_t x32t[2], xh[2], xht[2], a, b, partial, split, split_bytes, total;
 };
 
 NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
@@ -108,6 +111,8 @@ NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
   p.a = c.take(nn * cs);
   p.b = c.take(nn * cs);
   p.partial = c.take((size_t)batch * p.nblk * 4);
+  p.split_bytes = split_scratch(p.s, batch, cdt);
+  p.split = c.take(p.split_bytes);
   p.total = c.off;
   return p;
 }
@@ -115,7 +120,7 @@ NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
 struct GramPlan {
   Shape s;
   int32_t nblk;
-  size_t xh[2], xht[2], r, z, rz, q[2], partial, total;
+  size_t xh[2], xht[2], r, z, rz, q[2], partial, split, split_bytes, total;
 };
 
 GramPlan plan_gram(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
@@ -135,6 +140,8 @@ GramPlan plan_gram(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
   p.q[0] = c.take(nn * cs);
   p.q[1] = c.take(nn * cs);
   p.partial = c.take((size_t)batch * p.nblk * 4);
+  p.split_bytes = split_scratch(p.s, batch, cdt);
+  p.split = c.take(p.split_bytes);
   p.total = c.off;
   return p;
 }
@@ -199,10 +206,10 @@ enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3 };
 
 // Tile configurations (measured on MI355X, 8192^2 bf16): 256 x 256 tiles
 // with 16 waves of 64 x 64 (4 waves per SIMD hide LDS and MFMA latency; the
-// 64 accumulators per lane stay in VGPRs) when the problem has at least one
-// full round of such tiles for the 256 CUs; otherwise 128 x 128 tiles with
-// 4 waves of 64 x 64.  K slices are 64 bytes with two slices of register
-// prefetch.
+// 64 accumulators per lane stay in VGPRs; one block per CU) when the problem
+// has at least one full round of such tiles for the 256 CUs; otherwise
+// 128 x 128 tiles with 4 waves of 64 x 64 (two blocks per CU).  K slices are
+// 64 bytes with two slices of register prefetch.
 constexpr int kCUs = 256;
 
 int tri_blocks(int tiles) {
@@ -210,31 +217,95 @@ int tri_blocks(int tiles) {
   return tv / 2 * (tv + 1);
 }
 
+// How one product launch is laid out: tile configuration, tiles, and the
+// K split of the tiles past the last full round of resident blocks.
+struct LaunchPlan {
+  bool big;
+  int bm;
+  int32_t tiles_m, tiles_n, tpm;
+  int64_t nt, nfull, tail;
+  int32_t split;
+  size_t partial_bytes;
+};
+
+LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri, int32_t cdt) {
+  LaunchPlan l;
+  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t tiles256 = (tri ? (t256 + (M + 255) / 256) / 2 : t256) * batch;
+  l.big = tiles256 >= kCUs;
+  l.bm = l.big ? 256 : 128;
+  const int per_cu = l.big ? 1 : 2;
+  l.tiles_m = (int32_t)((M + l.bm - 1) / l.bm);
+  l.tiles_n = (int32_t)((N + l.bm - 1) / l.bm);
+  l.tpm = tri ? tri_blocks(l.tiles_m) : l.tiles_m * l.tiles_n;
+  l.nt = (int64_t)l.tpm * batch;
+  l.nfull = l.nt;
+  l.tail = 0;
+  l.split = 1;
+  const int64_t slots = (int64_t)kCUs * per_cu;
+  const int64_t rem = l.nt % slots;
+  const int64_t kslices = K / (cdt == MSIGN_F32 ? 16 : 32);
+  if (rem > 0) {
+    int64_t sp = slots / rem;
+    if (sp > kslices / 4) sp = kslices / 4;  // at least 4 K slices per part
+    if (sp >= 2) {
+      l.split = (int32_t)sp;
+      l.tail = rem;
+      l.nfull = l.nt - rem;
+    }
+  }
+  l.partial_bytes = (size_t)l.tail * l.split * l.bm * l.bm * 4;
+  return l;
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
-hipError_t launch_cfg(GemmParams q, int64_t batch, hipStream_t st) {
-  q.tiles_m = (q.M + BM - 1) / BM;
-  q.tiles_n = (q.N + BN - 1) / BN;
-  const unsigned gx = TRI ? (unsigned)tri_blocks(q.tiles_m) : (unsigned)(q.tiles_m * q.tiles_n);
-  if (gx == 0) return hipSuccess;
-  dim3 grid(gx, 1, (unsigned)batch);
-  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI><<<grid, WGM * WGN * 64, 0, st>>>(q);
+hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
+  q.tiles_m = l.tiles_m;
+  q.tiles_n = l.tiles_n;
+  q.tpm = l.tpm;
+  q.nfull = (int32_t)l.nfull;
+  q.split = l.split;
+  const int64_t blocks = l.nfull + l.tail * l.split;
+  if (blocks == 0) return hipSuccess;
+  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI><<<dim3((unsigned)blocks), WGM * WGN * 64, 0, st>>>(q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || l.tail == 0) return e;
+  gemm_nt_reduce_kernel<T, BM, BN, WGM, WGN, TRI><<<dim3((unsigned)l.tail), WGM * WGN * 64, 0, st>>>(q);
   return hipGetLastError();
 }
 
 template <typename T, bool TRI>
-hipError_t launch_nt_t(const GemmParams& q, int64_t batch, hipStream_t st) {
-  const int64_t t256 = (int64_t)((q.M + 255) / 256) * ((q.N + 255) / 256);
-  const int64_t tiles = (TRI ? (t256 + (q.M + 255) / 256) / 2 : t256) * batch;
-  if (tiles >= kCUs) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI>(q, batch, st);
-  return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI>(q, batch, st);
+hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
+  if (l.big) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI>(q, l, st);
+  return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI>(q, l, st);
 }
 
-hipError_t launch_nt(int32_t cdt, bool tri, const GemmParams& q, int64_t batch, hipStream_t st) {
-  switch (cdt) {
-    case MSIGN_BF16: return tri ? launch_nt_t<bf16_t, true>(q, batch, st) : launch_nt_t<bf16_t, false>(q, batch, st);
-    case MSIGN_F16: return tri ? launch_nt_t<f16_t, true>(q, batch, st) : launch_nt_t<f16_t, false>(q, batch, st);
-    default: return tri ? launch_nt_t<float, true>(q, batch, st) : launch_nt_t<float, false>(q, batch, st);
+// Launch one product.  `partial`/`partial_cap` is workspace for the K-split
+// tail; with too little of it the tail is computed whole instead.
+hipError_t launch_nt(int32_t cdt, bool tri, GemmParams q, int64_t batch, hipStream_t st,
+                     void* partial = nullptr, size_t partial_cap = 0) {
+  LaunchPlan l = plan_launch(q.M, q.N, q.K, batch, tri, cdt);
+  if (l.tail > 0 && (partial == nullptr || partial_cap < l.partial_bytes)) {
+    l.nfull = l.nt;
+    l.tail = 0;
+    l.split = 1;
   }
+  q.partial = static_cast<float*>(partial);
+  switch (cdt) {
+    case MSIGN_BF16: return tri ? launch_nt_t<bf16_t, true>(q, l, st) : launch_nt_t<bf16_t, false>(q, l, st);
+    case MSIGN_F16: return tri ? launch_nt_t<f16_t, true>(q, l, st) : launch_nt_t<f16_t, false>(q, l, st);
+    default: return tri ? launch_nt_t<float, true>(q, l, st) : launch_nt_t<float, false>(q, l, st);
+  }
+}
+
+// Largest K-split scratch any product of an NS or Gram call needs.
+size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt) {
+  size_t b = 0;
+  const LaunchPlan ls[3] = {plan_launch(s.np, s.np, s.mp, batch, true, cdt),
+                            plan_launch(s.np, s.np, s.np, batch, true, cdt),
+                            plan_launch(s.np, s.mp, s.np, batch, false, cdt)};
+  for (const LaunchPlan& l : ls) b = l.partial_bytes > b ? l.partial_bytes : b;
+  return b;
 }
 
 msign_status_t hip_fail(hipError_t e, const char* what) {
@@ -407,6 +478,7 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
   void* A = at(workspace, pl.a);
   void* B = at(workspace, pl.b);
   float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
+  void* split = at(workspace, pl.split);
 
   // X0: Xh (n x m), Xht and X32t (m x n, i.e. transposed relative to X)
   NormOut outs[3] = {
@@ -426,7 +498,7 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
       GemmParams g = gemm_base(xh[cur], s.mp, nm, xh[cur], s.mp, nm, s.np, s.np, s.mp, 1.f);
       add_out(g, A, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
       TimedLaunch tl(KC_SYRK, stream);
-      e = launch_nt(cdt, true, g, batch, stream);
+      e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "X X^T");
     }
     {  // B = c A A + b A
@@ -434,7 +506,7 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
       set_d(g, A, s.np, nn, cdt, b, true);
       add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
       TimedLaunch tl(KC_SQUARE, stream);
-      e = launch_nt(cdt, true, g, batch, stream);
+      e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "c A A + b A");
     }
     {  // X' = B X + a X
@@ -448,7 +520,7 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
         add_final_out(g, y, s, io_dtype);
       }
       TimedLaunch tl(KC_RECT, stream);
-      e = launch_nt(cdt, false, g, batch, stream);
+      e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "B X + a X");
     }
   }
@@ -491,6 +563,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
   void* RZ = at(workspace, pl.rz);
   void* Qb[2] = {at(workspace, pl.q[0]), at(workspace, pl.q[1])};
   float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
+  void* split = at(workspace, pl.split);
 
   NormOut outs[2] = {{xh[0], s.mp, nm, cdt, 0}, {xht[0], s.np, nm, cdt, 1}};
   st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 2, stream);
@@ -502,7 +575,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     GemmParams g = gemm_base(xh[cur], s.mp, nm, xh[cur], s.mp, nm, s.np, s.np, s.mp, 1.f);
     add_out(g, R, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
     TimedLaunch tl(KC_SYRK, stream);
-    e = launch_nt(cdt, true, g, batch, stream);
+    e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
     return e == hipSuccess ? MSIGN_OK : hip_fail(e, "R = X X^T");
   };
   // tri product: out = P Q^T + beta D  (all n x n, symmetric)
@@ -513,7 +586,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     add_out(g, out, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
     if (out2) add_out(g, out2, s.np, nn, cdt, false, s.np, s.np, diag2, s.n, true);
     TimedLaunch tl(KC_SQUARE, stream);
-    e = launch_nt(cdt, true, g, batch, stream);
+    e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
     return e == hipSuccess ? MSIGN_OK : hip_fail(e, what);
   };
 
@@ -545,7 +618,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
       add_out(g, xht[cur ^ 1], s.np, nm, cdt, true, s.np, s.mp, 0.f, 0, true);
       {
         TimedLaunch tl(KC_RECT, stream);
-        e = launch_nt(cdt, false, g, batch, stream);
+        e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes);
         if (e != hipSuccess) return hip_fail(e, "restart X <- Q X");
       }
       cur ^= 1;
@@ -558,18 +631,29 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     GemmParams g = gemm_base(Qb[qc], s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np, 1.f);
     add_final_out(g, y, s, io_dtype);
     TimedLaunch tl(KC_RECT, stream);
-    e = launch_nt(cdt, false, g, batch, stream);
+    e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes);
     if (e != hipSuccess) return hip_fail(e, "y = Q X");
   }
   return MSIGN_OK;
 }
 
+namespace {
+// syrk_xxt workspace: [zero-padded copy of x, only when k is not a multiple
+// of 64][K-split scratch for the last round of tiles, optional]
+size_t syrk_pad_bytes(int64_t batch, int64_t n, int64_t k, int32_t dtype) {
+  if (k % kPad == 0) return 0;
+  return align256((size_t)batch * pad_up(n) * pad_up(k) * dt_size(dtype));
+}
+size_t syrk_split_bytes(int64_t batch, int64_t n, int64_t k, int32_t dtype) {
+  return align256(plan_launch(n, n, pad_up(k), batch, true, dtype).partial_bytes);
+}
+}  // namespace
+
 size_t syrk_xxt_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t dtype) {
   if (batch < 0 || n < 0 || k < 0 || n > kMaxDim || k > kMaxDim || batch > kMaxBatch || !dt_valid(dtype))
     return (size_t)-1;
   if (batch == 0 || n == 0 || k == 0) return 0;
-  if (k % kPad == 0) return 0;
-  return align256((size_t)batch * pad_up(n) * pad_up(k) * dt_size(dtype));
+  return syrk_pad_bytes(batch, n, k, dtype) + syrk_split_bytes(batch, n, k, dtype);
 }
 
 msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_t k, int32_t dtype,
@@ -592,17 +676,27 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_
   if (x && k > 0 && overlap(x, (size_t)batch * n * k * es, c, c_bytes))
     return fail(MSIGN_ERR_ALIAS, "c overlaps x");
   if (d && overlap(d, c_bytes, c, c_bytes)) return fail(MSIGN_ERR_ALIAS, "c overlaps d");
-  const size_t need = syrk_xxt_workspace_bytes(batch, n, k, dtype);
   // the product kernel reads K in whole 64-element slices from 16-byte
   // aligned rows; other inputs are first copied into a padded buffer
   const bool direct = (k % kPad == 0) && aligned(x, 16);
+  const size_t pad_need = direct ? 0 : align256((size_t)batch * pad_up(n) * pad_up(k) * es);
   if (!direct && k > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(MSIGN_ERR_WORKSPACE, "workspace is null or smaller than the required " + std::to_string(need) + " bytes");
+    if (!workspace || workspace_bytes < pad_need)
+      return fail(MSIGN_ERR_WORKSPACE, "workspace is null or smaller than the required " + std::to_string(pad_need) + " bytes");
+  }
+  if (workspace) {
     if (!aligned(workspace, 256)) return fail(MSIGN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (overlap(workspace, need, c, c_bytes) || overlap(workspace, need, x, (size_t)batch * n * k * es) ||
-        (d && overlap(workspace, need, d, c_bytes)))
+    if (overlap(workspace, workspace_bytes, c, c_bytes) ||
+        (x && k > 0 && overlap(workspace, workspace_bytes, x, (size_t)batch * n * k * es)) ||
+        (d && overlap(workspace, workspace_bytes, d, c_bytes)))
       return fail(MSIGN_ERR_ALIAS, "workspace overlaps x, c or d");
+  }
+  // K-split scratch (optional): whatever workspace follows the padded copy
+  void* split = nullptr;
+  size_t split_cap = 0;
+  if (workspace && workspace_bytes > pad_need) {
+    split = at(workspace, pad_need);
+    split_cap = workspace_bytes - pad_need;
   }
 
   const void* P = x;
@@ -632,7 +726,7 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_
   if (d && beta != 0.f) set_d(g, d, n, n * n, dtype, beta, (n % 4 == 0) && aligned(d, 4 * es));
   add_out(g, c, n, n * n, dtype, false, n, n, gamma, n, vec_c);
   TimedLaunch tl(KC_SYRK, stream);
-  hipError_t e = launch_nt(dtype, true, g, batch, stream);
+  hipError_t e = launch_nt(dtype, true, g, batch, stream, split, split_cap);
   if (e != hipSuccess) return hip_fail(e, "syrk_xxt");
   return MSIGN_OK;
 }
