@@ -30,6 +30,9 @@
  *     NaN/Inf in the input propagate; an all-zero matrix maps to zero.
  *   - Bit stability: results do not depend on timing (no atomics, fixed
  *     reduction orders); the same call on the same device gives the same bits.
+ *     The launch layout (tile size, K split of the last round of tiles)
+ *     depends on the problem's shape including `batch`, so one matrix may
+ *     differ in the last bits between calls with different batch sizes.
  *   - Concurrency: calls are thread-safe and may run on different streams as
  *     long as they do not share output or workspace buffers.
  */

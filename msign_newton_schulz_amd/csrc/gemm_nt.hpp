@@ -177,73 +177,78 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int L, int64_t& bz,
   }
 }
 
-// Epilogue on the fp32 accumulators of one tile (lane layout of the 16x16
-// MFMA): alpha*acc + beta*D (D read through its transpose Dt[j][i], four
-// consecutive values per lane), a per-output diagonal term, then each
-// output's stores.  Triangle mode stores the tile and its mirror; in a
-// diagonal tile only i <= j is kept.
+// Epilogue of one 16 x 16 fragment (fm, fn) of wave `wave` of a tile, from
+// its fp32 accumulators in the MFMA lane layout (lane l, register r holds
+// row 4 (l / 16) + r, column l % 16): alpha*acc + beta*D (D read through its
+// transpose Dt[j][i], four consecutive values per lane), a per-output
+// diagonal term, then each output's stores.  Triangle mode stores the tile
+// and its mirror; in a diagonal tile only i <= j is kept.
 template <int BM, int BN, int WGM, int WGN, bool TRI>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int64_t bz, int ti, int tj,
-                                         const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16]) {
+__device__ __forceinline__ void epilogue_frag(const GemmParams& p, int64_t bz, int ti, int tj,
+                                              int wave, int fm, int fn, const f32x4& a) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int wm = wave / WGN, wn = wave % WGN;
   const int m0 = ti * BM, n0 = tj * BN;
   const bool diag_tile = TRI && (ti == tj);
-#pragma clang loop unroll(full)
-  for (int fm = 0; fm < FM; ++fm) {
-#pragma clang loop unroll(full)
-    for (int fn = 0; fn < FN; ++fn) {
-      const int i0 = m0 + wm * WM + fm * 16 + 4 * (lane >> 4);
-      const int j = n0 + wn * WN + fn * 16 + (lane & 15);
-      float v[4];
+  const int i0 = m0 + wm * WM + fm * 16 + 4 * (lane >> 4);
+  const int j = n0 + wn * WN + fn * 16 + (lane & 15);
+  float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = p.alpha * acc[fm][fn][r];
-      if (p.Dt != nullptr && j < p.N && i0 < p.M) {
-        float d[4];
-        const int64_t base = bz * p.sd + (int64_t)j * p.ldd + i0;
-        if (p.d_vec_ok && i0 + 3 < p.M) {
-          load_vec4(p.Dt, base, p.d_dtype, d);
-        } else {
+  for (int r = 0; r < 4; ++r) v[r] = p.alpha * a[r];
+  if (p.Dt != nullptr && j < p.N && i0 < p.M) {
+    float d[4];
+    const int64_t base = bz * p.sd + (int64_t)j * p.ldd + i0;
+    if (p.d_vec_ok && i0 + 3 < p.M) {
+      load_vec4(p.Dt, base, p.d_dtype, d);
+    } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) d[r] = (i0 + r < p.M) ? load_as_f32(p.Dt, base + r, p.d_dtype) : 0.f;
-        }
+      for (int r = 0; r < 4; ++r) d[r] = (i0 + r < p.M) ? load_as_f32(p.Dt, base + r, p.d_dtype) : 0.f;
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += p.beta * d[r];
+    for (int r = 0; r < 4; ++r) v[r] += p.beta * d[r];
+  }
+  for (int o = 0; o < p.nout; ++o) {
+    const OutSpec& os = p.out[o];
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + r;
+      w[r] = v[r] + ((i == j && i < os.diag_lim) ? os.diag : 0.f);
+    }
+    if (j >= os.cols_lim) continue;
+    if (TRI || !os.transposed) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        if (i < os.rows_lim && (!diag_tile || i <= j)) store_elem(os, bz, i, j, w[r]);
       }
-      for (int o = 0; o < p.nout; ++o) {
-        const OutSpec& os = p.out[o];
-        float w[4];
+    }
+    if (TRI || os.transposed) {
+      // element (i, j) goes to ptr[j * ld + i]; in triangle mode this is the mirror
+      const int64_t base = bz * os.bstride + (int64_t)j * os.ld + i0;
+      if (os.vec_ok && !diag_tile && i0 + 3 < os.rows_lim) {
+        store_vec4(os.ptr, base, os.dtype, w);
+      } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
-          w[r] = v[r] + ((i == j && i < os.diag_lim) ? os.diag : 0.f);
-        }
-        if (j >= os.cols_lim) continue;
-        if (TRI || !os.transposed) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = i0 + r;
-            if (i < os.rows_lim && (!diag_tile || i <= j)) store_elem(os, bz, i, j, w[r]);
-          }
-        }
-        if (TRI || os.transposed) {
-          // element (i, j) goes to ptr[j * ld + i]; in triangle mode this is the mirror
-          const int64_t base = bz * os.bstride + (int64_t)j * os.ld + i0;
-          if (os.vec_ok && !diag_tile && i0 + 3 < os.rows_lim) {
-            store_vec4(os.ptr, base, os.dtype, w);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = i0 + r;
-              if (i < os.rows_lim && (!diag_tile || i < j)) store_from_f32(os.ptr, base + r, os.dtype, w[r]);
-            }
-          }
+          if (i < os.rows_lim && (!diag_tile || i < j)) store_from_f32(os.ptr, base + r, os.dtype, w[r]);
         }
       }
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN, bool TRI>
+__device__ __forceinline__ void epilogue(const GemmParams& p, int64_t bz, int ti, int tj,
+                                         const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
+                                         int wave) {
+#pragma clang loop unroll(full)
+  for (int fm = 0; fm < BM / WGM / 16; ++fm)
+#pragma clang loop unroll(full)
+    for (int fn = 0; fn < BN / WGN / 16; ++fn)
+      epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm, fn, acc[fm][fn]);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
@@ -418,43 +423,58 @@ gemm_nt_kernel(const GemmParams p) {
   }
 
   if (part >= 0) {  // partial sums of this K range, one f32x4 per thread and fragment
-    f32x4* dst = reinterpret_cast<f32x4*>(p.partial) + (int64_t)unit * (FM * FN * NT);
+    // layout [split tile][wave][part][fragment][lane]: each wave writes, and
+    // the reduce pass reads, one contiguous run per part
+    const int t = unit / p.split;
+    f32x4* dst = reinterpret_cast<f32x4*>(p.partial) +
+                 (((int64_t)t * (WGM * WGN) + wave) * p.split + part) * (FM * FN * 64) + lane;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * NT + tid] = acc[fm][fn];
+      for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * 64] = acc[fm][fn];
     return;
   }
-  epilogue<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, acc);
+  epilogue<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, acc, wave);
 }
 
-// Second pass for split tiles: one block per tile adds its parts' partial
-// sums in part order (fixed, so the result is bit-stable) and runs the same
-// epilogue as a whole tile.
+// Second pass for split tiles.  Block (t, w) takes wave w's fragments of
+// split tile t; its wave q handles fragment row fm = q: it adds the tile's
+// parts in part order (fixed, so the result is bit-stable) and runs the
+// epilogue of those fragments.  Splitting the work this way keeps many
+// partial-sum loads in flight per lane (the pass is latency-bound).
 template <typename T, int BM, int BN, int WGM, int WGN, bool TRI>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+__global__ void __launch_bounds__(BM / WGM / 16 * 64)
 gemm_nt_reduce_kernel(const GemmParams p) {
-  constexpr int NT = WGM * WGN * 64;
+  constexpr int WG = WGM * WGN;
   constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
-  const int t = blockIdx.x;
+  constexpr int FF = FM * FN * 64;  // f32x4 per wave and part
+  const int t = blockIdx.x / WG, w = blockIdx.x % WG;
+  const int fm = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int64_t bz;
   int ti, tj;
   if (!tile_of<TRI>(p, p.nfull + t, bz, ti, tj)) return;
-  const int tid = threadIdx.x;
-  const f32x4* src = reinterpret_cast<const f32x4*>(p.partial) + (int64_t)t * p.split * (FM * FN * NT);
-  f32x4 acc[FM][FN];
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.partial) + ((int64_t)t * WG + w) * p.split * FF +
+                     fm * FN * 64 + lane;
+  f32x4 acc[FN];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int fn = 0; fn < FN; ++fn) acc[fn] = src[fn * 64];
+  int sp = 1;
+  for (; sp + 4 <= p.split; sp += 4) {
+    f32x4 v[4][FN];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = src[(fm * FN + fn) * NT + tid];
-  for (int sp = 1; sp < p.split; ++sp) {
-    const f32x4* s2 = src + (int64_t)sp * (FM * FN * NT);
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+      for (int fn = 0; fn < FN; ++fn) v[u][fn] = src[(int64_t)(sp + u) * FF + fn * 64];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] += s2[(fm * FN + fn) * NT + tid];
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fn] += v[u][fn];
   }
-  epilogue<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, acc);
+  for (; sp < p.split; ++sp)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] += src[(int64_t)sp * FF + fn * 64];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, w, fm, fn, acc[fn]);
 }
 
 }  // namespace msign

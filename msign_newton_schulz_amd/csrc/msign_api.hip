@@ -208,9 +208,12 @@ enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3 };
 // with 16 waves of 64 x 64 (4 waves per SIMD hide LDS and MFMA latency; the
 // 64 accumulators per lane stay in VGPRs; one block per CU) when the problem
 // has at least one full round of such tiles for the 256 CUs; otherwise
-// 128 x 128 tiles with 4 waves of 64 x 64 (two blocks per CU).  K slices are
-// 64 bytes with two slices of register prefetch.
+// 128 x 128 tiles with 4 waves of 64 x 64 (two blocks per CU) if those fill
+// the CUs, else 64 x 64 tiles of one wave (latency-bound problems: more,
+// shorter tiles instead of long K splits).  K slices are 64 bytes with two
+// slices of register prefetch.
 constexpr int kCUs = 256;
+constexpr int kSplitMax = 8;
 
 int tri_blocks(int tiles) {
   const int tv = tiles + (tiles & 1);
@@ -220,8 +223,7 @@ int tri_blocks(int tiles) {
 // How one product launch is laid out: tile configuration, tiles, and the
 // K split of the tiles past the last full round of resident blocks.
 struct LaunchPlan {
-  bool big;
-  int bm;
+  int bm;  // tile edge: 256, 128 or 64
   int32_t tiles_m, tiles_n, tpm;
   int64_t nt, nfull, tail;
   int32_t split;
@@ -230,11 +232,18 @@ struct LaunchPlan {
 
 LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri, int32_t cdt) {
   LaunchPlan l;
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t tiles256 = (tri ? (t256 + (M + 255) / 256) / 2 : t256) * batch;
-  l.big = tiles256 >= kCUs;
-  l.bm = l.big ? 256 : 128;
-  const int per_cu = l.big ? 1 : 2;
+  auto tiles_at = [&](int64_t e) {
+    const int64_t tm = (M + e - 1) / e, t = tm * ((N + e - 1) / e);
+    return (tri ? (t + tm) / 2 : t) * batch;
+  };
+  // the largest tile that still gives every CU a tile; 64 x 64 tiles (one
+  // wave) when even 128 x 128 tiles leave CUs idle
+  l.bm = tiles_at(256) >= kCUs ? 256 : (tiles_at(128) >= kCUs ? 128 : 64);
+  // Blocks per CU that splitting the last round aims for (measured): one
+  // 16-wave block of 256 x 256 keeps a CU busy; 4-wave 128 x 128 blocks
+  // gain from two per CU and the latency-bound one-wave 64 x 64 blocks from
+  // four.
+  const int per_cu = l.bm == 256 ? 1 : (l.bm == 128 ? 2 : 4);
   l.tiles_m = (int32_t)((M + l.bm - 1) / l.bm);
   l.tiles_n = (int32_t)((N + l.bm - 1) / l.bm);
   l.tpm = tri ? tri_blocks(l.tiles_m) : l.tiles_m * l.tiles_n;
@@ -247,6 +256,7 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   const int64_t kslices = K / (cdt == MSIGN_F32 ? 16 : 32);
   if (rem > 0) {
     int64_t sp = slots / rem;
+    if (sp > kSplitMax) sp = kSplitMax;     // bounds the partial-sum traffic
     if (sp > kslices / 4) sp = kslices / 4;  // at least 4 K slices per part
     if (sp >= 2) {
       l.split = (int32_t)sp;
@@ -270,14 +280,16 @@ hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
   gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI><<<dim3((unsigned)blocks), WGM * WGN * 64, 0, st>>>(q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.tail == 0) return e;
-  gemm_nt_reduce_kernel<T, BM, BN, WGM, WGN, TRI><<<dim3((unsigned)l.tail), WGM * WGN * 64, 0, st>>>(q);
+  gemm_nt_reduce_kernel<T, BM, BN, WGM, WGN, TRI>
+      <<<dim3((unsigned)(l.tail * WGM * WGN)), BM / WGM / 16 * 64, 0, st>>>(q);
   return hipGetLastError();
 }
 
 template <typename T, bool TRI>
 hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
-  if (l.big) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI>(q, l, st);
-  return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI>(q, l, st);
+  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI>(q, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI>(q, l, st);
+  return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI>(q, l, st);
 }
 
 // Launch one product.  `partial`/`partial_cap` is workspace for the K-split
