@@ -97,38 +97,6 @@ __device__ __forceinline__ void store_elem(const OutSpec& os, int64_t bz, int64_
   store_from_f32(os.ptr, bz * os.bstride + r * os.ld + c, os.dtype, v);
 }
 
-// Store w[0..3] to ptr[base + 0..3] (consecutive elements) in one vector store.
-__device__ __forceinline__ void store_vec4(void* ptr, int64_t base, int32_t dt, const float* w) {
-  if (dt == DT_F32) {
-    f32x4 v = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<f32x4*>(static_cast<float*>(ptr) + base) = v;
-  } else {
-    uint32_t lo, hi;
-    if (dt == DT_BF16) {
-      lo = f32_to_bf16_bits(w[0]) | ((uint32_t)f32_to_bf16_bits(w[1]) << 16);
-      hi = f32_to_bf16_bits(w[2]) | ((uint32_t)f32_to_bf16_bits(w[3]) << 16);
-    } else {
-      lo = f32_to_f16_bits(w[0]) | ((uint32_t)f32_to_f16_bits(w[1]) << 16);
-      hi = f32_to_f16_bits(w[2]) | ((uint32_t)f32_to_f16_bits(w[3]) << 16);
-    }
-    u32x2 v = {lo, hi};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(ptr) + base) = v;
-  }
-}
-
-__device__ __forceinline__ void load_vec4(const void* ptr, int64_t base, int32_t dt, float* d) {
-  if (dt == DT_F32) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(ptr) + base);
-    d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-  } else {
-    u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(ptr) + base);
-    uint16_t h[4] = {(uint16_t)(v[0] & 0xffff), (uint16_t)(v[0] >> 16),
-                     (uint16_t)(v[1] & 0xffff), (uint16_t)(v[1] >> 16)};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) d[r] = dt == DT_BF16 ? bf16_bits_to_f32(h[r]) : f16_bits_to_f32(h[r]);
-  }
-}
-
 // 16-byte chunk position inside an LDS row of CPR chunks: XOR swizzle so
 // that the 16 lanes reading one fragment column (16 consecutive rows, same
 // logical chunk) hit distinct bank groups.

@@ -7,11 +7,12 @@
 //     one partial.  Fixed slice boundaries and trees make the sum bit-stable.
 //  2. normalize_kernel: grid (64x64 tiles of the padded input, batch).  Each
 //     block re-sums that matrix's partials in a fixed order, forms the scale
-//     1/sqrt(sum + eps) in fp32, loads its input tile into LDS, and writes
-//     every requested copy of the scaled tile: in the input's orientation or
-//     transposed (read back column-wise from LDS so both stores coalesce), in
-//     fp32 or the compute dtype.  Tiles cover the padded extents, so padding
-//     rows and columns of every copy are written as zeros.
+//     1/sqrt(sum + eps) in fp32, loads its input tile into LDS (16-byte loads
+//     when the input's rows allow), and writes every requested copy of the
+//     scaled tile: in the input's orientation or transposed (read back
+//     column-wise from LDS), in fp32 or the compute dtype, four consecutive
+//     elements per store.  Tiles cover the padded extents (multiples of 64),
+//     so padding rows and columns of every copy are written as zeros.
 //     A null partial pointer means scale 1 (a plain cast/transpose/pad).
 #pragma once
 
@@ -112,28 +113,69 @@ normalize_kernel(const NormParams p) {
     if (tid == 0) s_scale = scale;
   }
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = tid & 63, ty = tid >> 6;
   const int64_t xb = b * p.rows * p.cols;
-  for (int rr = ty; rr < 64; rr += 4) {
-    const int64_t r = r0 + rr, c = c0 + tx;
-    tile[rr][tx] = (r < p.rows && c < p.cols) ? load_as_f32(p.x, xb + r * p.cols + c, p.x_dtype) : 0.f;
+  const bool wide16 = p.x_dtype != DT_F32;
+  const int per_chunk = wide16 ? 8 : 4;  // elements per 16-byte chunk
+  const bool vec_in = (p.cols % per_chunk) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.x) & 15) == 0;
+  if (vec_in) {
+    // rows hold whole chunks: a chunk is either inside the matrix or not
+    const int cpr = 64 / per_chunk;
+    for (int q = tid; q < 64 * cpr; q += 256) {
+      const int rr = q / cpr, cc = (q % cpr) * per_chunk;
+      const int64_t r = r0 + rr, c = c0 + cc;
+      float v[8];
+      if (r < p.rows && c < p.cols) {
+        const int64_t e = xb + r * p.cols + c;
+        if (wide16) {
+          const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint16_t lo = u[k] & 0xffff, hi = u[k] >> 16;
+            v[2 * k] = p.x_dtype == DT_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
+            v[2 * k + 1] = p.x_dtype == DT_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
+          }
+        } else {
+          const f32x4 u = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = u[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = 0.f;
+      }
+      for (int k = 0; k < per_chunk; ++k) tile[rr][cc + k] = v[k];
+    }
+  } else {
+    const int tx = tid & 63, ty = tid >> 6;
+    for (int rr = ty; rr < 64; rr += 4) {
+      const int64_t r = r0 + rr, c = c0 + tx;
+      tile[rr][tx] = (r < p.rows && c < p.cols) ? load_as_f32(p.x, xb + r * p.cols + c, p.x_dtype) : 0.f;
+    }
   }
   __syncthreads();
   const float sc = s_scale;
   for (int o = 0; o < p.nout; ++o) {
     const NormOut& os = p.out[o];
-    if (!os.transposed) {
-      for (int rr = ty; rr < 64; rr += 4) {
-        const int r = r0 + rr, c = c0 + tx;
-        if (r < p.rows_pad && c < p.cols_pad)
-          store_from_f32(os.ptr, b * os.bstride + (int64_t)r * os.ld + c, os.dtype, tile[rr][tx] * sc);
+    // quad q: row (or, transposed, column) q / 16 of the tile, 4 elements
+    // starting at 4 (q % 16) along the other index
+    for (int q = tid; q < 1024; q += 256) {
+      const int u = q >> 4, w0 = (q & 15) * 4;
+      float v[4];
+      int64_t base;
+      bool inside;
+      if (!os.transposed) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = tile[u][w0 + k] * sc;
+        base = b * os.bstride + (int64_t)(r0 + u) * os.ld + c0 + w0;
+        inside = r0 + u < p.rows_pad && c0 + w0 + 3 < p.cols_pad;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = tile[w0 + k][u] * sc;
+        base = b * os.bstride + (int64_t)(c0 + u) * os.ld + r0 + w0;
+        inside = c0 + u < p.cols_pad && r0 + w0 + 3 < p.rows_pad;
       }
-    } else {
-      for (int cc = ty; cc < 64; cc += 4) {
-        const int c = c0 + cc, r = r0 + tx;
-        if (r < p.rows_pad && c < p.cols_pad)
-          store_from_f32(os.ptr, b * os.bstride + (int64_t)c * os.ld + r, os.dtype, tile[tx][cc] * sc);
-      }
+      if (inside) store_vec4(os.ptr, base, os.dtype, v);
     }
   }
 }
