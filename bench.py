@@ -60,6 +60,45 @@ def class_flops(n, m):
     return {"xxt": float(m) * n * n, "square": float(n) ** 3, "rect": 2.0 * m * n * n}
 
 
+# Counter summary of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, scaled by the same counters on a plain copy of known size).  Its
+# traffic figure is reported only while the kernel sources hash to the value
+# recorded with it; after any change to them it is stale and `traffic` is null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_rect_8192x8192_bf16_traffic.md")
+KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "msign_api.hip")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "msign_newton_schulz_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kclass):
+    """Bytes per launch from the committed counter summary, or None if there
+    is none for this workload and kernel class or the sources changed."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if (fields.get("workload") != workload or fields.get("kernel class") != kclass
+            or fields.get("source sha256") != kernel_source_hash()):
+        return None
+    try:
+        return float(fields["traffic bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,11 +202,23 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
             else:
                 M.msign_gram_ns(x, compute_dtype=tdt, restart_after=restarts, out=y, workspace=ws)
 
+    probe = None
+    if with_timing:
+        # one untimed step with every class timed: the per-class breakdown
+        # and the dominant product class
+        M.kernel_timing(True)
+        one_step()
+        torch.cuda.synchronize()
+        probe = M.read_kernel_timing()
+        M.kernel_timing(False)
     for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
+    dom = None
     if with_timing:
-        M.kernel_timing(True)
+        # the timed region brackets only the dominant class's launches
+        dom = max(("xxt", "square", "rect"), key=lambda k: probe[k][0])
+        M.kernel_timing(True, classes=[dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -206,10 +257,9 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
     if ktime is not None:
         per = {}
         for k in ("normalize", "xxt", "square", "rect"):
-            tot, cnt = ktime[k]
+            tot, cnt = probe[k]
             per[k] = {"total_ms": tot, "launches": cnt, "avg_us": 1e3 * tot / cnt if cnt else None}
-        rec["kernels"] = per
-        dom = max(("xxt", "square", "rect"), key=lambda k: ktime[k][0])
+        rec["kernels_one_step"] = per
         tot, cnt = ktime[dom]
         if cnt:
             # every group's call makes the same number of launches of a class;
@@ -220,7 +270,8 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
             ach = flops_per_launch / avg_s / 1e12
             rec["roofline"] = {"bound": "mfma", "kernel": f"gemm_nt_kernel ({dom})", "achieved": ach,
                                "peak": PEAK_TFLOPS[cdt], "unit": "TFLOP/s",
-                               "frac": ach / PEAK_TFLOPS[cdt], "traffic": None,
+                               "frac": ach / PEAK_TFLOPS[cdt],
+                               "traffic": recorded_traffic(workload, dom),
                                "avg_launch_us": avg_s * 1e6,
                                "algorithmic_flops_per_launch": flops_per_launch}
     if with_cpu:

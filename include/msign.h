@@ -176,17 +176,22 @@ const char* msign_version(void);
 
 /*
  * Per-kernel-class timing with HIP events, for measurement only.
- * While enabled, every launch made by the calls above is bracketed by a pair
- * of events recorded on the call's stream; msign_kernel_timing_read() waits
- * for them, adds their durations to per-class totals and clears the queue.
+ * While enabled for a class, every launch of that class made by the calls
+ * above is bracketed by a pair of events recorded on the call's stream;
+ * msign_kernel_timing_read() waits for them, adds their durations to
+ * per-class totals and clears the queue.
  * Classes: 0 = normalise (sum of squares + scale/cast), 1 = X X^T (triangle),
  * 2 = n x n triangle products (A^2 / Gram R, Q, Z, RZ updates), 3 = the
  * rectangular product (B X, Q X).
- *   msign_kernel_timing_enable   1 enables, 0 disables (and frees events);
- *                                returns MSIGN_ERR_HIP if events cannot be made.
+ *   msign_kernel_timing_enable   mask of classes to time (bit k = class k,
+ *                                MSIGN_KCLASS_ALL for all; a nonzero mask also
+ *                                resets the totals); 0 disables (and frees
+ *                                events).  Bits beyond the classes give
+ *                                MSIGN_ERR_ARG.
  *   msign_kernel_timing_read     fills total_ms[4] and launches[4] (HOST).
  */
 #define MSIGN_KCLASS_COUNT 4
+#define MSIGN_KCLASS_ALL 0xF
 msign_status_t msign_kernel_timing_enable(int32_t enable);
 msign_status_t msign_kernel_timing_read(double* total_ms, int64_t* launches);
 

@@ -228,9 +228,15 @@ def syrk_xxt(x: torch.Tensor, alpha: float = 1.0, d: Optional[torch.Tensor] = No
     return c
 
 
-def kernel_timing(enable: bool):
-    """Turn per-kernel-class HIP event timing on or off (measurement only)."""
-    _check(_load().msign_kernel_timing_enable(1 if enable else 0))
+def kernel_timing(enable: bool, classes=None):
+    """Turn per-kernel-class HIP event timing on or off (measurement only).
+    `classes` limits it to some of KCLASSES (default: all)."""
+    mask = 0
+    if enable:
+        names = KCLASSES if classes is None else classes
+        for c in names:
+            mask |= 1 << KCLASSES.index(c)
+    _check(_load().msign_kernel_timing_enable(mask))
 
 
 def read_kernel_timing():

@@ -155,7 +155,7 @@ struct Pending {
 
 struct Timing {
   std::mutex mu;
-  std::atomic<bool> enabled{false};
+  std::atomic<uint32_t> mask{0};  // classes being timed (bit k = class k)
   std::vector<Pending> pending;
   std::vector<hipEvent_t> pool;
   double total_ms[MSIGN_KCLASS_COUNT] = {0, 0, 0, 0};
@@ -185,7 +185,7 @@ struct TimedLaunch {
   hipEvent_t start = nullptr, stop = nullptr;
   TimedLaunch(int kc, hipStream_t s) : kclass(kc), stream(s) {
     Timing& t = timing();
-    if (!t.enabled.load()) return;
+    if (!((t.mask.load() >> kc) & 1u)) return;
     std::lock_guard<std::mutex> g(t.mu);
     start = pool_event(t);
     stop = pool_event(t);
@@ -763,15 +763,17 @@ const char* msign_version(void) { return "msign 0.1.0 gfx950"; }
 msign_status_t msign_kernel_timing_enable(int32_t enable) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (enable) {
+  const uint32_t mask = (uint32_t)enable & ((1u << MSIGN_KCLASS_COUNT) - 1u);
+  if (enable < 0 || (uint32_t)enable != mask) return fail(MSIGN_ERR_ARG, "unknown kernel class in mask");
+  if (mask) {
     for (int k = 0; k < MSIGN_KCLASS_COUNT; ++k) {
       t.total_ms[k] = 0;
       t.launches[k] = 0;
     }
-    t.enabled.store(true);
+    t.mask.store(mask);
     return MSIGN_OK;
   }
-  t.enabled.store(false);
+  t.mask.store(0);
   for (auto& p : t.pending) {
     (void)hipEventSynchronize(p.stop);
     t.pool.push_back(p.start);

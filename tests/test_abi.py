@@ -151,6 +151,14 @@ def test_timing_read_rejects_null():
     assert lib.msign_kernel_timing_read(None, None) == 1
 
 
+def test_timing_mask_validation():
+    lib = _lib()
+    assert lib.msign_kernel_timing_enable(0x10) == 1
+    assert lib.msign_kernel_timing_enable(-1) == 1
+    assert lib.msign_kernel_timing_enable(0b1000) == 0   # rect only
+    assert lib.msign_kernel_timing_enable(0) == 0
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     _lib()
