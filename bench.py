@@ -202,20 +202,18 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
             else:
                 M.msign_gram_ns(x, compute_dtype=tdt, restart_after=restarts, out=y, workspace=ws)
 
-    probe = None
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    probe = dom = None
     if with_timing:
-        # one untimed step with every class timed: the per-class breakdown
-        # and the dominant product class
+        # one more untimed step with every class timed: the per-class
+        # breakdown and the dominant product class
         M.kernel_timing(True)
         one_step()
         torch.cuda.synchronize()
         probe = M.read_kernel_timing()
         M.kernel_timing(False)
-    for _ in range(warmup):
-        one_step()
-    torch.cuda.synchronize()
-    dom = None
-    if with_timing:
         # the timed region brackets only the dominant class's launches
         dom = max(("xxt", "square", "rect"), key=lambda k: probe[k][0])
         M.kernel_timing(True, classes=[dom])
