@@ -219,10 +219,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int64_t bz, int ti
       epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm, fn, acc[fm][fn]);
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
-__global__ void __launch_bounds__(WGM * WGN * 64)
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW>
+__global__ void __launch_bounds__(WGM * WGN * KW * 64)
 gemm_nt_kernel(const GemmParams p) {
-  constexpr int NT = WGM * WGN * 64;
+  constexpr int NT = WGM * WGN * KW * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int ESZ = Elem<T>::size;
@@ -230,17 +230,22 @@ gemm_nt_kernel(const GemmParams p) {
   constexpr int CPR = BKB / 16;     // chunks per row of one K slice
   constexpr int KTE = CPR * CE;     // elements per K slice
   constexpr int KSUB = CPR / 4;     // MFMA K sub-steps per slice (4 lane groups)
-  constexpr int ACH = BM * CPR / NT, BCH = BN * CPR / NT;
+  constexpr int ACH = BM * CPR * KW / NT, BCH = BN * CPR * KW / NT;
   static_assert(CPR == 4 || CPR == 8, "K slice must be 64 or 128 bytes");
+  // KW > 1: KW waves share one tile (WGM = WGN = 1), wave w taking K slices
+  // w, w + KW, ...; one load step brings KW consecutive slices, thread group
+  // s of a step moving slice s (so NT / CPR must equal the tile edge)
+  static_assert(KW == 1 || (WGM == 1 && WGN == 1 && BM == BN && NT / CPR == BM), "K-split waves");
   static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile/thread mismatch");
   static_assert(!TRI || BM == BN, "triangle mode needs square tiles");
   static_assert(NST >= 1 && NST <= 3, "one to three K slices of register prefetch");
 
-  __shared__ u32x4 lds[2][(BM + BN) * CPR];
+  __shared__ u32x4 lds[2][KW * (BM + BN) * CPR];  // [stage][A slices, then B slices]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int kw = KW > 1 ? tid >> 6 : 0;    // K share of this wave
+  const int wave = KW > 1 ? 0 : tid >> 6;  // position of this wave in the tile
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- tile (or K part of a tile) of this block ----
@@ -280,8 +285,8 @@ gemm_nt_kernel(const GemmParams p) {
   const int kcol = ch0 * CE;
   const int a_base = (row0 * (int)p.ldp + kcol) * ESZ;
   const int b_base = (row0 * (int)p.ldq + kcol) * ESZ;
-  const int a_step = RSTEP * (int)p.ldp * ESZ;
-  const int b_step = RSTEP * (int)p.ldq * ESZ;
+  const int a_step = KW > 1 ? KTE * ESZ : RSTEP * (int)p.ldp * ESZ;
+  const int b_step = KW > 1 ? KTE * ESZ : RSTEP * (int)p.ldq * ESZ;
   const int lds_w = row0 * CPR + swz<CPR>(row0, ch0);  // + s * RSTEP * CPR
 
 
@@ -302,7 +307,7 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
     for (int s = 0; s < ACH; ++s) lds[buf][lds_w + s * RSTEP * CPR] = src[s];
 #pragma unroll
-    for (int s = 0; s < BCH; ++s) lds[buf][BM * CPR + lds_w + s * RSTEP * CPR] = src[ACH + s];
+    for (int s = 0; s < BCH; ++s) lds[buf][KW * BM * CPR + lds_w + s * RSTEP * CPR] = src[ACH + s];
   };
 
   f32x4 acc[FM][FN];
@@ -325,14 +330,14 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int row = wm * WM + fm * 16 + (lane & 15);
-        a[fm] = lds[buf][row * CPR + swz<CPR>(row, ch)];
+        a[fm] = lds[buf][(kw * BM + row) * CPR + swz<CPR>(row, ch)];
       }
       if constexpr (kAllFrags) {
         u32x4 b[FN];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int row = wn * WN + fn * 16 + (lane & 15);
-          b[fn] = lds[buf][(BM + row) * CPR + swz<CPR>(row, ch)];
+          b[fn] = lds[buf][(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -342,7 +347,7 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int row = wn * WN + fn * 16 + (lane & 15);
-          const u32x4 b = lds[buf][(BM + row) * CPR + swz<CPR>(row, ch)];
+          const u32x4 b = lds[buf][(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) Mma<T>::run(acc[fm][fn], a[fm], b);
         }
@@ -363,31 +368,66 @@ gemm_nt_kernel(const GemmParams p) {
     kt0 = (int)((int64_t)part * KT / p.split);
     nk = (int)((int64_t)(part + 1) * KT / p.split) - kt0;
   }
+  // steps of KW slices; wave kw computes slice j * KW + kw of step j when
+  // that slice is in range
+  const int ns = (nk + KW - 1) / KW;
   u32x4 stg[NST][ACH + BCH];
   gload(stg[0], kt0 * KTE);
-  if constexpr (NST >= 2) gload(stg[1], (kt0 + 1) * KTE);
-  if constexpr (NST >= 3) gload(stg[2], (kt0 + 2) * KTE);
-  if (nk > 0) lstore(stg[0], 0);
+  if constexpr (NST >= 2) gload(stg[1], (kt0 + KW) * KTE);
+  if constexpr (NST >= 3) gload(stg[2], (kt0 + 2 * KW) * KTE);
+  if (ns > 0) lstore(stg[0], 0);
   __syncthreads();
   auto iter = [&](int j, auto S) {
     constexpr int s = decltype(S)::value;  // j % NST
-    gload(stg[s], (kt0 + j + NST) * KTE);
-    compute(j & 1);
-    if (j + 1 < nk) lstore(stg[(s + 1) % NST], (j + 1) & 1);
+    gload(stg[s], (kt0 + (j + NST) * KW) * KTE);
+    if (KW == 1 || j * KW + kw < nk) compute(j & 1);
+    if (j + 1 < ns) lstore(stg[(s + 1) % NST], (j + 1) & 1);
     __syncthreads();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, (1 % NST)>;
   using I2 = std::integral_constant<int, (2 % NST)>;
   int j = 0;
-  for (; j + NST <= nk; j += NST) {
+  for (; j + NST <= ns; j += NST) {
     iter(j, I0{});
     if constexpr (NST >= 2) iter(j + 1, I1{});
     if constexpr (NST >= 3) iter(j + 2, I2{});
   }
-  if (j < nk) iter(j, I0{});
+  if (j < ns) iter(j, I0{});
   if constexpr (NST >= 3) {
-    if (j + 1 < nk) iter(j + 1, I1{});
+    if (j + 1 < ns) iter(j + 1, I1{});
+  }
+
+  if constexpr (KW > 1) {
+    // The K shares' accumulators meet in LDS (the last iteration ended with
+    // a barrier, so the ring is free); wave q then adds fragment row fm = q
+    // over the shares in share order (fixed, so bit-stable) and finishes it.
+    static_assert(KW == FM, "one fragment row per wave");
+    static_assert(KW * FM * FN * 64 * 16 <= (int)sizeof(lds), "LDS holds every share");
+    f32x4* red = reinterpret_cast<f32x4*>(&lds[0][0]);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) red[((kw * FM + fm) * FN + fn) * 64 + lane] = acc[fm][fn];
+    __syncthreads();
+    const int fm = kw;
+    f32x4 sum[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      sum[fn] = red[(fm * FN + fn) * 64 + lane];
+#pragma unroll
+      for (int q = 1; q < KW; ++q) sum[fn] += red[((q * FM + fm) * FN + fn) * 64 + lane];
+    }
+    if (part >= 0) {  // same partial layout as below, written by fragment row
+      const int t = unit / p.split;
+      f32x4* dst = reinterpret_cast<f32x4*>(p.partial) + ((int64_t)t * p.split + part) * (FM * FN * 64) + lane;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * 64] = sum[fn];
+      return;
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, 0, fm, fn, sum[fn]);
+    return;
   }
 
   if (part >= 0) {  // partial sums of this K range, one f32x4 per thread and fragment

@@ -241,9 +241,10 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   l.bm = tiles_at(256) >= kCUs ? 256 : (tiles_at(128) >= kCUs ? 128 : 64);
   // Blocks per CU that splitting the last round aims for (measured): one
   // 16-wave block of 256 x 256 keeps a CU busy; 4-wave 128 x 128 blocks
-  // gain from two per CU and the latency-bound one-wave 64 x 64 blocks from
-  // four.
-  const int per_cu = l.bm == 256 ? 1 : (l.bm == 128 ? 2 : 4);
+  // gain from two per CU.  A 64 x 64 tile is already shared along K by its
+  // four waves.
+  const int per_cu = l.bm == 128 ? 2 : 1;
+  const int kwaves = l.bm == 64 ? 4 : 1;
   l.tiles_m = (int32_t)((M + l.bm - 1) / l.bm);
   l.tiles_n = (int32_t)((N + l.bm - 1) / l.bm);
   l.tpm = tri ? tri_blocks(l.tiles_m) : l.tiles_m * l.tiles_n;
@@ -257,7 +258,7 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   if (rem > 0) {
     int64_t sp = slots / rem;
     if (sp > kSplitMax) sp = kSplitMax;     // bounds the partial-sum traffic
-    if (sp > kslices / 4) sp = kslices / 4;  // at least 4 K slices per part
+    if (sp > kslices / (4 * kwaves)) sp = kslices / (4 * kwaves);  // >= 4 K slices per wave
     if (sp >= 2) {
       l.split = (int32_t)sp;
       l.tail = rem;
@@ -268,7 +269,7 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   return l;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI>
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW>
 hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
   q.tiles_m = l.tiles_m;
   q.tiles_n = l.tiles_n;
@@ -277,7 +278,7 @@ hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
   q.split = l.split;
   const int64_t blocks = l.nfull + l.tail * l.split;
   if (blocks == 0) return hipSuccess;
-  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI><<<dim3((unsigned)blocks), WGM * WGN * 64, 0, st>>>(q);
+  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI, KW><<<dim3((unsigned)blocks), WGM * WGN * KW * 64, 0, st>>>(q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.tail == 0) return e;
   gemm_nt_reduce_kernel<T, BM, BN, WGM, WGN, TRI>
@@ -287,9 +288,9 @@ hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
 
 template <typename T, bool TRI>
 hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
-  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI>(q, l, st);
-  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI>(q, l, st);
-  return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI>(q, l, st);
+  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 64, 2, TRI, 1>(q, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI, 1>(q, l, st);
+  return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI, 4>(q, l, st);
 }
 
 // Launch one product.  `partial`/`partial_cap` is workspace for the K-split
