@@ -93,7 +93,9 @@ size_t msign_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
  *   steps          1..MSIGN_MAX_STEPS.
  *   coeffs         HOST pointer to steps*3 floats (a_t, b_t, c_t per row,
  *                  [KX] §解开约束), or NULL for (3.4445, -4.7750, 2.0315)
- *                  at every step.  Read before the call returns.
+ *                  at every step.  Read before the call returns.  A step
+ *                  with c_t == 0 (cubic, [KX] §迭代计算) skips the A A
+ *                  product: X <- a_t X + b_t A X.
  *   eps            >= 0, added to sum X^2 before the square root (1e-20 in
  *                  [KX] §参考实现).
  *   workspace      device, at least msign_ns_workspace_bytes(...) bytes,

@@ -514,7 +514,10 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
       e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "X X^T");
     }
-    {  // B = c A A + b A
+    // A cubic step (c = 0, "msign算子的Newton-Schulz迭代（上）" §迭代计算) has
+    // B = b A: no A A product, and the next product takes A scaled by b.
+    const bool cubic = (c == 0.f);
+    if (!cubic) {  // B = c A A + b A
       GemmParams g = gemm_base(A, s.np, nn, A, s.np, nn, s.np, s.np, s.np, c);
       set_d(g, A, s.np, nn, cdt, b, true);
       add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
@@ -523,7 +526,8 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
       if (e != hipSuccess) return hip_fail(e, "c A A + b A");
     }
     {  // X' = B X + a X
-      GemmParams g = gemm_base(B, s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np, 1.f);
+      GemmParams g = gemm_base(cubic ? A : B, s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np,
+                               cubic ? b : 1.f);
       set_d(g, x32t[cur], s.np, nm, MSIGN_F32, a, true);
       if (t + 1 < steps) {
         add_out(g, x32t[nxt], s.np, nm, MSIGN_F32, true, s.np, s.mp, 0.f, 0, true);

@@ -159,6 +159,31 @@ def test_ns_small_fp32_workload_against_exact_and_oracle():
     assert O.max_rel_fro_error(y, O.exact_msign(xs)) <= bound + 1e-4
 
 
+@pytest.mark.parametrize("cdt,tol", [("f32", 1e-4), ("bf16", 2e-2)])
+def test_ns_cubic_steps_skip_the_square(cdt, tol):
+    """c_t = 0 steps (nil9.net's third-order tables) take the path without
+    A A: parity with the oracle, and the A^2 class is launched once per
+    quintic step only."""
+    M = require_gpu()
+    announce(f"msign_ns cubic and mixed tables compute={cdt}")
+    # fp32 compute is checked with fp32 input and output (a bf16 output alone
+    # carries ~2^-9 relative rounding)
+    x = _input(192, 448, "f32" if cdt == "f32" else "bf16", 91, batch=2)
+    cubic = [[1.5, -0.5, 0.0]] * 8
+    mixed = [[3.4445, -4.7750, 2.0315]] * 3 + [[1.99, -0.99, 0.0]] * 2 + [[1.5, -0.5, 0.0]]
+    for table in (cubic, mixed):
+        M.kernel_timing(True)
+        y = M.msign_ns(x.cuda(), steps=len(table), coeffs=table, compute_dtype=TORCH_DT[cdt])
+        torch.cuda.synchronize()
+        counts = M.read_kernel_timing()
+        M.kernel_timing(False)
+        err = O.max_rel_fro_error(f64(y), O.ns(f64(x), coeffs=np.array(table), steps=len(table)))
+        assert err <= tol, err
+        quintic = sum(1 for r in table if r[2] != 0.0)
+        assert counts["square"][1] == quintic
+        assert counts["rect"][1] == len(table)
+
+
 @pytest.mark.parametrize("cdt", ["bf16", "f16"])
 def test_ns_spiked_alpha4_workload(cdt):
     """1024x4096 bf16, N(0, 0.02^2) + rank-8 spike (full size)."""

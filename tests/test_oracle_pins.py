@@ -146,12 +146,32 @@ def test_svd_msign_rank_deficient_and_zero():
 # --- Newton-Schulz iteration -------------------------------------------------
 
 @pytest.mark.parametrize("shape", [(16, 40), (40, 16), (24, 24), (3, 50)])
-@pytest.mark.parametrize("table", ["keller", "youjiacheng_t6", "dion_t5"])
+@pytest.mark.parametrize("table", ["keller", "youjiacheng_t6", "dion_t5", "bernstein_cubic", "nil9_cubic"])
 def test_ns_equals_per_singular_value_composition(shape, table):
     # kexue.fm 10922 §原理分析 / Gram NS Proposition 1
     rows, t = TABLES[table]
     m = _rand(shape, 21, 3.0)
     assert np.allclose(O.ns_single(m, rows, t), O.spectral_ns_single(m, rows, t), atol=1e-12)
+
+
+@pytest.mark.parametrize("table", ["bernstein_cubic", "nil9_cubic"])
+def test_cubic_tables_fix_one(table):
+    # nil9.net, third-order iteration: f(1) = a + b = 1 and |f'(1)| = |a + 3b| < 1
+    rows, _ = TABLES[table]
+    a, b, c = rows[0]
+    assert c == 0.0 and abs(a + b - 1.0) < 1e-15 and abs(a + 3 * b) < 1.0
+
+
+def test_cubic_iteration_converges_to_polar_factor():
+    # The classical cubic Newton-Schulz step x -> (3x - x^3) / 2 maps (0, 1]
+    # into itself and converges to 1 (quadratically near 1), so enough steps
+    # from the Frobenius-normalised start give U V^T of a full-rank matrix.
+    rows, _ = TABLES["bernstein_cubic"]
+    m = _rand((20, 50), 31)
+    y = O.ns_single(m, tuple(rows[0]), 40)
+    assert np.allclose(y, O.svd_msign(m), atol=1e-10)
+    # and of the transposed (tall) input
+    assert np.allclose(O.ns_single(m.T, tuple(rows[0]), 40), O.svd_msign(m).T, atol=1e-10)
 
 
 def test_ns_on_spd_matches_eigendecomposition():
