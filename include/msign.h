@@ -107,6 +107,25 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows,
                         void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/*
+ * msign_ns_ex - msign_ns with option flags (msign_ns is msign_ns_ex with
+ * flags = 0; both use msign_ns_workspace_bytes).
+ *
+ *   MSIGN_NS_IMPROVED_INIT  improved initial normalisation ([KX] §改良初值):
+ *       on the first step, with A = X X^T and A2 = A A of the Frobenius-
+ *       normalised X0, the iterate is further divided by
+ *       s = (sum A2^2 + eps)^(1/8) = ||(X0 X0^T)^2||_F^(1/4) <= ||X0||_F,
+ *       i.e. X1 = a X0/s + (b A/s^2 + c A2/s^4) X0/s.  A2 is formed even when
+ *       c_1 = 0.  Later steps are unchanged.
+ *   Other bits are MSIGN_ERR_ARG.
+ */
+#define MSIGN_NS_IMPROVED_INIT 1u
+msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows,
+                           int64_t cols, int32_t io_dtype, int32_t compute_dtype,
+                           int32_t steps, const float* coeffs, float eps,
+                           uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Bytes of device workspace msign_gram_ns needs; see msign_ns_workspace_bytes. */
 size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
                                      int32_t compute_dtype);

@@ -53,6 +53,8 @@ def _load():
     lib.syrk_xxt_workspace_bytes.restype = sz
     lib.msign_ns.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, fp, f, vp, sz, vp]
     lib.msign_ns.restype = ctypes.c_int
+    lib.msign_ns_ex.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, fp, f, ctypes.c_uint32, vp, sz, vp]
+    lib.msign_ns_ex.restype = ctypes.c_int
     lib.msign_gram_ns.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, fp, f, ip, i32, vp, sz, vp]
     lib.msign_gram_ns.restype = ctypes.c_int
     lib.syrk_xxt.argtypes = [vp, vp, i64, i64, i64, i32, f, vp, f, f, vp, sz, vp]
@@ -144,12 +146,17 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+IMPROVED_INIT = 1  # MSIGN_NS_IMPROVED_INIT
+
+
 def msign_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-20,
              compute_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+             workspace: Optional[torch.Tensor] = None,
+             improved_init: bool = False) -> torch.Tensor:
     """Standard quintic Newton-Schulz msign over the last two dims (C ABI
-    `msign_ns`).  `coeffs`: None (Keller constants), one (a, b, c) triple or
-    a table of `steps` rows.  Returns a tensor shaped and typed like `x`."""
+    `msign_ns`, or `msign_ns_ex` with MSIGN_NS_IMPROVED_INIT when
+    `improved_init`).  `coeffs`: None (Keller constants), one (a, b, c) triple
+    or a table of `steps` rows.  Returns a tensor shaped and typed like `x`."""
     _check_cuda(x, out, workspace)
     lib = _load()
     x = x.contiguous()
@@ -162,8 +169,9 @@ def msign_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-20,
     ws = _workspace(nbytes, x.device, workspace)
     carr = _coeff_array(coeffs, steps)
     with torch.cuda.device(x.device):
-        st = lib.msign_ns(x.data_ptr(), y.data_ptr(), batch, rows, cols, io, cdt, steps,
-                          carr, float(eps), ws.data_ptr(), ws.numel(), _stream_handle(x.device))
+        st = lib.msign_ns_ex(x.data_ptr(), y.data_ptr(), batch, rows, cols, io, cdt, steps,
+                             carr, float(eps), IMPROVED_INIT if improved_init else 0,
+                             ws.data_ptr(), ws.numel(), _stream_handle(x.device))
     _check(st)
     return y
 

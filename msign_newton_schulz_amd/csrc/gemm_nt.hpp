@@ -68,6 +68,14 @@ struct GemmParams {
   // fixed order by gemm_nt_reduce_kernel.
   int32_t tpm, nfull, split;
   float* partial;
+  // Optional per-matrix factor computed on the device: every value
+  // (alpha acc + beta D) is multiplied by vscale[4 bz].
+  const float* vscale;
+  // Optional, triangle products: sums of acc^2 over each tile (off-diagonal
+  // tiles counted twice, for their mirror), one per (tile, wave, fragment
+  // row) at sumsq[((bz tpm + tile) WG + wave) FM + fm]; the slots of the
+  // padding blocks of the folded triangle are not written.
+  float* sumsq;
 };
 
 template <typename T> struct Mma;
@@ -152,8 +160,8 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int L, int64_t& bz,
 // diagonal term, then each output's stores.  Triangle mode stores the tile
 // and its mirror; in a diagonal tile only i <= j is kept.
 template <int BM, int BN, int WGM, int WGN, bool TRI>
-__device__ __forceinline__ void epilogue_frag(const GemmParams& p, int64_t bz, int ti, int tj,
-                                              int wave, int fm, int fn, const f32x4& a) {
+__device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, int ti, int tj,
+                                               int wave, int fm, int fn, const f32x4& a) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   const int lane = threadIdx.x & 63;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -175,6 +183,11 @@ __device__ __forceinline__ void epilogue_frag(const GemmParams& p, int64_t bz, i
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] += p.beta * d[r];
+  }
+  if (p.vscale != nullptr) {
+    const float f = p.vscale[4 * bz];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] *= f;
   }
   for (int o = 0; o < p.nout; ++o) {
     const OutSpec& os = p.out[o];
@@ -206,17 +219,35 @@ __device__ __forceinline__ void epilogue_frag(const GemmParams& p, int64_t bz, i
       }
     }
   }
+  return a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+}
+
+// Sum of v over the wave (fixed butterfly, so bit-stable), stored by lane 0.
+__device__ __forceinline__ void wave_sum_store(float v, float* dst) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0) *dst = v;
+}
+
+// Slot of (tile L, wave, fragment row fm) among the acc^2 sums.
+template <int BM, int WGM, int WGN>
+__device__ __forceinline__ float* sumsq_slot(const GemmParams& p, int L, int wave, int fm) {
+  return p.sumsq + ((int64_t)L * (WGM * WGN) + wave) * (BM / WGM / 16) + fm;
 }
 
 template <int BM, int BN, int WGM, int WGN, bool TRI>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int64_t bz, int ti, int tj,
+__device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz, int ti, int tj,
                                          const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
                                          int wave) {
+  const float w2 = (TRI && ti != tj) ? 2.f : 1.f;
 #pragma clang loop unroll(full)
-  for (int fm = 0; fm < BM / WGM / 16; ++fm)
+  for (int fm = 0; fm < BM / WGM / 16; ++fm) {
+    float sq = 0.f;
 #pragma clang loop unroll(full)
     for (int fn = 0; fn < BN / WGN / 16; ++fn)
-      epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm, fn, acc[fm][fn]);
+      sq += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm, fn, acc[fm][fn]);
+    if (TRI && p.sumsq != nullptr) wave_sum_store(w2 * sq, sumsq_slot<BM, WGM, WGN>(p, L, wave, fm));
+  }
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW>
@@ -425,8 +456,11 @@ gemm_nt_kernel(const GemmParams p) {
       for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * 64] = sum[fn];
       return;
     }
+    float sq = 0.f;
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, 0, fm, fn, sum[fn]);
+    for (int fn = 0; fn < FN; ++fn) sq += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, 0, fm, fn, sum[fn]);
+    if (TRI && p.sumsq != nullptr)
+      wave_sum_store((ti != tj ? 2.f : 1.f) * sq, sumsq_slot<BM, WGM, WGN>(p, L, 0, fm));
     return;
   }
 
@@ -442,7 +476,7 @@ gemm_nt_kernel(const GemmParams p) {
       for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * 64] = acc[fm][fn];
     return;
   }
-  epilogue<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, acc, wave);
+  epilogue<BM, BN, WGM, WGN, TRI>(p, L, bz, ti, tj, acc, wave);
 }
 
 // Second pass for split tiles.  Block (t, w) takes wave w's fragments of
@@ -481,8 +515,65 @@ gemm_nt_reduce_kernel(const GemmParams p) {
   for (; sp < p.split; ++sp)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] += src[(int64_t)sp * FF + fn * 64];
+  float sq = 0.f;
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, w, fm, fn, acc[fn]);
+  for (int fn = 0; fn < FN; ++fn) sq += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, w, fm, fn, acc[fn]);
+  if (TRI && p.sumsq != nullptr)
+    wave_sum_store((ti != tj ? 2.f : 1.f) * sq, sumsq_slot<BM, WGM, WGN>(p, p.nfull + t, w, fm));
+}
+
+// Improved initial normalisation ("msign算子的Newton-Schulz迭代（上）"
+// §改良初值): after the first A = X X^T and A2 = A A, the iterate is divided
+// by s = (||A2||_F^2 + eps)^(1/8), the fourth root of ||(X X^T)^2||_F.
+//
+// init_scale_kernel: one block per matrix adds that matrix's acc^2 slots of
+// the A A launch `q` (the slot layout of GemmParams::sumsq, `slots` per
+// tile, padding blocks of the folded triangle skipped) in a fixed order and
+// writes scales[4 bz + k] = s^-(1, 2, 4)[k].
+__global__ void __launch_bounds__(256)
+init_scale_kernel(const GemmParams q, int32_t slots, float eps, float* scales) {
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  float acc = 0.f;
+  for (int64_t i = tid; i < (int64_t)q.tpm * slots; i += 256) {
+    const int L = (int)(b * q.tpm + i / slots);
+    int64_t bz;
+    int ti, tj;
+    if (tile_of<true>(q, L, bz, ti, tj)) acc += q.sumsq[(int64_t)L * slots + i % slots];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  __shared__ float ws[4];
+  if ((tid & 63) == 0) ws[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    const float sum = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+    const float s = sqrtf(sqrtf(sqrtf(sum + eps)));
+    const float r = 1.f / s;
+    scales[4 * b] = r;
+    scales[4 * b + 1] = r * r;
+    scales[4 * b + 2] = (r * r) * (r * r);
+    scales[4 * b + 3] = 0.f;
+  }
+}
+
+// B <- (b s^-2) A + (c s^-4) B over `per` elements (a multiple of 4) of each
+// matrix: the first B = b A + c A2 of the normalised iterate, with A2 held
+// in B.  Four consecutive elements per thread.
+__global__ void __launch_bounds__(256)
+init_combine_kernel(const void* A, void* B, int64_t per, int32_t dt, float b, float c,
+                    const float* scales) {
+  const int64_t bz = blockIdx.y;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= per) return;
+  const float fa = b * scales[4 * bz + 1], fb = c * scales[4 * bz + 2];
+  const int64_t base = bz * per + e;
+  float va[4], vb[4], w[4];
+  load_vec4(A, base, dt, va);
+  load_vec4(B, base, dt, vb);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = fa * va[k] + fb * vb[k];
+  store_vec4(B, base, dt, w);
 }
 
 }  // namespace msign

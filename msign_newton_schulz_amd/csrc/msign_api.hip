@@ -71,8 +71,10 @@ Shape canon(int64_t rows, int64_t cols) {
   return s;
 }
 
-// K-split scratch of the products of one NS or Gram call (defined below).
+// K-split scratch of the products of one NS or Gram call, and the acc^2
+// slots of the first A A product (defined below).
 size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt);
+size_t init_sumsq_floats(const Shape& s, int64_t batch, int32_t cdt);
 
 int32_t norm_blocks(int64_t count) {
   int64_t nb = (count + 16383) / 16384;
@@ -93,7 +95,7 @@ struct Carver {
 struct NsPlan {
   Shape s;
   int32_t nblk;
-  size_t x32t[2], xh[2], xht[2], a, b, partial, split, split_bytes, total;
+  size_t x32t[2], xh[2], xht[2], a, b, partial, sumsq, scales, split, split_bytes, total;
 };
 
 NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
@@ -111,6 +113,8 @@ NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
   p.a = c.take(nn * cs);
   p.b = c.take(nn * cs);
   p.partial = c.take((size_t)batch * p.nblk * 4);
+  p.sumsq = c.take(init_sumsq_floats(p.s, batch, cdt) * 4);
+  p.scales = c.take((size_t)batch * 4 * 4);
   p.split_bytes = split_scratch(p.s, batch, cdt);
   p.split = c.take(p.split_bytes);
   p.total = c.off;
@@ -311,6 +315,14 @@ hipError_t launch_nt(int32_t cdt, bool tri, GemmParams q, int64_t batch, hipStre
   }
 }
 
+// acc^2 slots (one per tile, wave and fragment row) of the A A launch.
+int32_t sumsq_slots_per_tile(int bm) { return bm == 256 ? 16 * 4 : (bm == 128 ? 4 * 4 : 4); }
+
+size_t init_sumsq_floats(const Shape& s, int64_t batch, int32_t cdt) {
+  const LaunchPlan l = plan_launch(s.np, s.np, s.np, batch, true, cdt);
+  return (size_t)l.nt * sumsq_slots_per_tile(l.bm);
+}
+
 // Largest K-split scratch any product of an NS or Gram call needs.
 size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt) {
   size_t b = 0;
@@ -473,7 +485,17 @@ size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, 
 msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
                         int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
                         float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return msign_ns_ex(x, y, batch, rows, cols, io_dtype, compute_dtype, steps, coeffs, eps, 0u, workspace,
+                     workspace_bytes, stream);
+}
+
+msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
+                           int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
+                           float eps, uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   g_err.clear();
+  if (flags & ~(uint32_t)MSIGN_NS_IMPROVED_INIT) return fail(MSIGN_ERR_ARG, "unknown flag");
+  const bool improved = (flags & MSIGN_NS_IMPROVED_INIT) != 0;
   bool empty = false;
   msign_status_t st = check_common(x, y, batch, rows, cols, io_dtype, compute_dtype, steps, coeffs, eps, &empty);
   if (st != MSIGN_OK || empty) return st;
@@ -491,6 +513,8 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
   void* A = at(workspace, pl.a);
   void* B = at(workspace, pl.b);
   float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
+  float* sumsq = reinterpret_cast<float*>(at(workspace, pl.sumsq));
+  float* scales = reinterpret_cast<float*>(at(workspace, pl.scales));
   void* split = at(workspace, pl.split);
 
   // X0: Xh (n x m), Xht and X32t (m x n, i.e. transposed relative to X)
@@ -514,10 +538,36 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
       e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "X X^T");
     }
+    // Improved initial normalisation (§改良初值), first step only: A2 = A A
+    // into B with its acc^2 sums, s from them, B = (b/s^2) A + (c/s^4) A2,
+    // and the update below scaled by 1/s.
+    const bool rescale = improved && t == 0;
+    if (rescale) {
+      GemmParams g = gemm_base(A, s.np, nn, A, s.np, nn, s.np, s.np, s.np, 1.f);
+      add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
+      g.sumsq = sumsq;
+      {
+        TimedLaunch tl(KC_SQUARE, stream);
+        e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
+        if (e != hipSuccess) return hip_fail(e, "A A (first step)");
+      }
+      const LaunchPlan l = plan_launch(s.np, s.np, s.np, batch, true, cdt);
+      g.tiles_m = l.tiles_m;
+      g.tiles_n = l.tiles_n;
+      g.tpm = l.tpm;
+      TimedLaunch tl(KC_NORM, stream);
+      init_scale_kernel<<<dim3((unsigned)batch), 256, 0, stream>>>(g, sumsq_slots_per_tile(l.bm), eps, scales);
+      e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "init_scale_kernel");
+      const unsigned nb = (unsigned)((nn / 4 + 255) / 256);
+      init_combine_kernel<<<dim3(nb, (unsigned)batch), 256, 0, stream>>>(A, B, nn, cdt, b, c, scales);
+      e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "init_combine_kernel");
+    }
     // A cubic step (c = 0, "msign算子的Newton-Schulz迭代（上）" §迭代计算) has
     // B = b A: no A A product, and the next product takes A scaled by b.
-    const bool cubic = (c == 0.f);
-    if (!cubic) {  // B = c A A + b A
+    const bool cubic = (c == 0.f) && !rescale;
+    if (!cubic && !rescale) {  // B = c A A + b A
       GemmParams g = gemm_base(A, s.np, nn, A, s.np, nn, s.np, s.np, s.np, c);
       set_d(g, A, s.np, nn, cdt, b, true);
       add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
@@ -528,6 +578,7 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
     {  // X' = B X + a X
       GemmParams g = gemm_base(cubic ? A : B, s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np,
                                cubic ? b : 1.f);
+      if (rescale) g.vscale = scales;
       set_d(g, x32t[cur], s.np, nm, MSIGN_F32, a, true);
       if (t + 1 < steps) {
         add_out(g, x32t[nxt], s.np, nm, MSIGN_F32, true, s.np, s.mp, 0.f, 0, true);

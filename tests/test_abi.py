@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for want in ("msign_ns", "msign_gram_ns", "syrk_xxt", "msign_ns_workspace_bytes",
+    for want in ("msign_ns", "msign_ns_ex", "msign_gram_ns", "syrk_xxt", "msign_ns_workspace_bytes",
                  "msign_gram_ns_workspace_bytes", "syrk_xxt_workspace_bytes",
                  "msign_status_string", "msign_last_error", "msign_version",
                  "msign_kernel_timing_enable", "msign_kernel_timing_read"):
@@ -112,6 +112,15 @@ def test_ns_argument_errors_before_launch():
     # empty problems succeed without touching anything
     assert _ns(lib, batch=0, x=None, y=None, ws=None, wsb=0) == 0
     assert _ns(lib, rows=0, x=None, y=None, ws=None, wsb=0) == 0
+
+
+def test_ns_ex_rejects_unknown_flags():
+    lib = _lib()
+    args = (FAKE, FAKE, 1, 8, 16, 1, 1, 5, None, 1e-20)
+    assert lib.msign_ns_ex(*args, 2, FAKE2, 1 << 30, None) == 1
+    assert lib.msign_ns_ex(*args, 0x80000000, FAKE2, 1 << 30, None) == 1
+    # a valid flag still goes through the other checks (too small a workspace)
+    assert lib.msign_ns_ex(*args, 1, FAKE2, 16, None) == 4
 
 
 def _gram(lib, restarts, n_restarts, steps=5, **kw):

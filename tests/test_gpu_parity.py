@@ -184,6 +184,44 @@ def test_ns_cubic_steps_skip_the_square(cdt, tol):
         assert counts["rect"][1] == len(table)
 
 
+@pytest.mark.parametrize("rows,cols,batch,cdt,tol", [
+    (160, 352, 2, "f32", 1e-4),     # 64x64 tiles
+    (352, 96, 3, "f32", 1e-4),      # tall input
+    (1024, 4096, 1, "bf16", 2e-2),  # 1024x4096 spiked-workload shape
+    (2048, 2048, 8, "bf16", 2e-2),  # 256x256 tiles with a K-split last round
+])
+def test_ns_improved_init(rows, cols, batch, cdt, tol):
+    """The improved initial normalisation ("msign算子的Newton-Schulz迭代（上）"
+    §改良初值) against the oracle's version of it; sampled matrices of the
+    8-matrix batch."""
+    M = require_gpu()
+    announce(f"msign_ns improved init {batch}x{rows}x{cols} compute={cdt}")
+    x = _input(rows, cols, "f32" if cdt == "f32" else "bf16", 300 + rows, batch=batch)
+    y = M.msign_ns(x.cuda(), compute_dtype=TORCH_DT[cdt], improved_init=True)
+    y_plain = M.msign_ns(x.cuda(), compute_dtype=TORCH_DT[cdt])
+    y_again = M.msign_ns(x.cuda(), compute_dtype=TORCH_DT[cdt], improved_init=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_again)
+    for i in sorted({0, batch - 1}):
+        ref = O.ns_improved_init(f64(x[i]))
+        err = O.max_rel_fro_error(f64(y[i]), ref)
+        assert err <= tol
+        # the extra division changes the result (s < 1 strictly for rank > 1):
+        # the plain iteration is much further from this reference
+        assert O.max_rel_fro_error(f64(y_plain[i]), ref) > 2 * max(err, tol / 10)
+
+
+def test_ns_improved_init_with_cubic_first_step():
+    M = require_gpu()
+    announce("msign_ns improved init, cubic table")
+    x = _input(128, 320, "f32", 404, batch=2)
+    table = [[1.5, -0.5, 0.0]] * 6
+    y = M.msign_ns(x.cuda(), steps=6, coeffs=table, compute_dtype=torch.float32, improved_init=True)
+    torch.cuda.synchronize()
+    ref = O.ns_improved_init(f64(x), coeffs=np.array(table), steps=6)
+    assert O.max_rel_fro_error(f64(y), ref) <= 1e-4
+
+
 @pytest.mark.parametrize("cdt", ["bf16", "f16"])
 def test_ns_spiked_alpha4_workload(cdt):
     """1024x4096 bf16, N(0, 0.02^2) + rank-8 spike (full size)."""
