@@ -33,9 +33,11 @@ METRIC = "msign matrices/s and effective TFLOP/s (% bf16 MFMA peak), T=5 NS, 1 G
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 HBM_GBS = 8000.0
 
-# name -> (workload, method, compute dtype, restarts)
+# name -> (workload, method, compute dtype, restarts); "ns_init" is standard NS
+# with the improved initial normalisation
 CASES = {
     "c3_ns_bf16": ("c3_8192x8192_bf16", "ns", "bf16", ()),
+    "c3_ns_init_bf16": ("c3_8192x8192_bf16", "ns_init", "bf16", ()),
     "c1_ns_f32": ("c1_128x256_f32", "ns", "f32", ()),
     "c1_ns_bf16": ("c1_128x256_f32", "ns", "bf16", ()),
     "c2_ns_bf16": ("c2_1024x4096_bf16", "ns", "bf16", ()),
@@ -162,6 +164,8 @@ def cpu_baseline(wl, method, sample_seconds=30.0):
             t0 = time.perf_counter()
             if method == "ns":
                 O.ns_single(m, steps=steps_run)
+            elif method == "ns_init":
+                O.ns_improved_init_single(m, steps=steps_run)
             else:
                 O.gram_ns_single(m, steps=steps_run, restart_after=(2,) if steps_run > 2 else ())
             dt = time.perf_counter() - t0
@@ -191,14 +195,14 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
     wss = []
     for x in xs:
         b, r, c = x.shape
-        nb = (M.ns_workspace_bytes(b, r, c, tdt) if method == "ns"
+        nb = (M.ns_workspace_bytes(b, r, c, tdt) if method.startswith("ns")
               else M.gram_ns_workspace_bytes(b, r, c, tdt))
         wss.append(torch.empty(max(nb, 1), dtype=torch.uint8, device=dev))
 
     def one_step():
         for x, y, ws in zip(xs, outs, wss):
-            if method == "ns":
-                M.msign_ns(x, compute_dtype=tdt, out=y, workspace=ws)
+            if method.startswith("ns"):
+                M.msign_ns(x, compute_dtype=tdt, out=y, workspace=ws, improved_init=(method == "ns_init"))
             else:
                 M.msign_gram_ns(x, compute_dtype=tdt, restart_after=restarts, out=y, workspace=ws)
 
@@ -246,7 +250,7 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cdt, "data": "synthetic",
-        "config": {"workload": workload, "case": name, "method": "msign_" + ("ns" if method == "ns" else "gram_ns"),
+        "config": {"workload": workload, "case": name, "method": {"ns": "msign_ns", "ns_init": "msign_ns_ex(IMPROVED_INIT)", "gram": "msign_gram_ns"}[method],
                    "shapes": shapes, "T": 5, "compute": cdt, "restart_after": list(restarts),
                    "parallelism": "single GPU"},
         "effective_tflops": eff_tflops,
