@@ -155,13 +155,15 @@ __device__ __forceinline__ bool tile_of(const GemmParams& p, int L, int64_t& bz,
 
 // Epilogue of one 16 x 16 fragment (fm, fn) of wave `wave` of a tile, from
 // its fp32 accumulators in the MFMA lane layout (lane l, register r holds
-// row 4 (l / 16) + r, column l % 16): alpha*acc + beta*D (D read through its
-// transpose Dt[j][i], four consecutive values per lane), a per-output
-// diagonal term, then each output's stores.  Triangle mode stores the tile
-// and its mirror; in a diagonal tile only i <= j is kept.
+// row 4 (l / 16) + r, column l % 16) and the four D values of those rows
+// (already loaded): alpha*acc + beta*D, times the per-matrix factor if any,
+// a per-output diagonal term, then each output's stores.  Triangle mode
+// stores the tile and its mirror; in a diagonal tile only i <= j is kept.
+// Returns this lane's sum of acc^2 over the fragment.
 template <int BM, int BN, int WGM, int WGN, bool TRI>
 __device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, int ti, int tj,
-                                               int wave, int fm, int fn, const f32x4& a) {
+                                               int wave, int fm, int fn, const f32x4& a,
+                                               const float (&d)[4]) {
   constexpr int WM = BM / WGM, WN = BN / WGN;
   const int lane = threadIdx.x & 63;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -171,19 +173,7 @@ __device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, 
   const int j = n0 + wn * WN + fn * 16 + (lane & 15);
   float v[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = p.alpha * a[r];
-  if (p.Dt != nullptr && j < p.N && i0 < p.M) {
-    float d[4];
-    const int64_t base = bz * p.sd + (int64_t)j * p.ldd + i0;
-    if (p.d_vec_ok && i0 + 3 < p.M) {
-      load_vec4(p.Dt, base, p.d_dtype, d);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d[r] = (i0 + r < p.M) ? load_as_f32(p.Dt, base + r, p.d_dtype) : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] += p.beta * d[r];
-  }
+  for (int r = 0; r < 4; ++r) v[r] = p.alpha * a[r] + p.beta * d[r];
   if (p.vscale != nullptr) {
     const float f = p.vscale[4 * bz];
 #pragma unroll
@@ -222,6 +212,83 @@ __device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, 
   return a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
 }
 
+// The D values (read through Dt[j][i], four consecutive i per lane) of NR
+// fragment rows fm0.. of wave `wave`; zeros where there is no D or it is out
+// of bounds.  When the tile lies inside D and rows allow vector loads, all
+// NR * FN loads are issued before any is used (one round trip, not one per
+// fragment); otherwise element loads with bounds checks.
+template <int BM, int BN, int WGM, int WGN, int NR>
+__device__ __forceinline__ void epilogue_load_d(const GemmParams& p, int64_t bz, int ti, int tj, int wave,
+                                                int fm0, float (&d)[NR * (BN / WGN / 16)][4]) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, FN = WN / 16, NF = NR * FN;
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int m0 = ti * BM, n0 = tj * BN;
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[f][r] = 0.f;
+  if (p.Dt == nullptr) return;
+  auto base_of = [&](int f) {
+    const int i0 = m0 + wm * WM + (fm0 + f / FN) * 16 + 4 * (lane >> 4);
+    const int j = n0 + wn * WN + (f % FN) * 16 + (lane & 15);
+    return bz * p.sd + (int64_t)j * p.ldd + i0;
+  };
+  if (p.d_vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+    if (p.d_dtype == DT_F32) {
+      f32x4 t[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) t[f] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.Dt) + base_of(f));
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[f][r] = t[f][r];
+    } else {
+      u32x2 t[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) t[f] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.Dt) + base_of(f));
+      const bool bf = p.d_dtype == DT_BF16;
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t h = (uint16_t)(t[f][r >> 1] >> (16 * (r & 1)));
+          d[f][r] = bf ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int i0 = m0 + wm * WM + (fm0 + f / FN) * 16 + 4 * (lane >> 4);
+    const int j = n0 + wn * WN + (f % FN) * 16 + (lane & 15);
+    if (j < p.N) {
+      const int64_t base = base_of(f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[f][r] = (i0 + r < p.M) ? load_as_f32(p.Dt, base + r, p.d_dtype) : 0.f;
+    }
+  }
+}
+
+// Epilogue of NR fragment rows fm0.. of wave `wave` (acc[f] is fragment
+// (fm0 + f / FN, f % FN)); sq[k] gets this lane's acc^2 sum of row fm0 + k.
+template <int BM, int BN, int WGM, int WGN, bool TRI, int NR>
+__device__ __forceinline__ void epilogue_rows(const GemmParams& p, int64_t bz, int ti, int tj, int wave,
+                                              int fm0, const f32x4 (&acc)[NR * (BN / WGN / 16)],
+                                              float (&sq)[NR]) {
+  constexpr int FN = BN / WGN / 16;
+  float d[NR * FN][4];
+  epilogue_load_d<BM, BN, WGM, WGN, NR>(p, bz, ti, tj, wave, fm0, d);
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    sq[k] = 0.f;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      sq[k] += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm0 + k, fn, acc[k * FN + fn],
+                                                   d[k * FN + fn]);
+  }
+}
+
 // Sum of v over the wave (fixed butterfly, so bit-stable), stored by lane 0.
 __device__ __forceinline__ void wave_sum_store(float v, float* dst) {
 #pragma unroll
@@ -239,14 +306,22 @@ template <int BM, int BN, int WGM, int WGN, bool TRI>
 __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz, int ti, int tj,
                                          const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
                                          int wave) {
+  constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
+  // fragment rows whose D loads share a round trip: two, except in the
+  // 16-wave tile, whose 128-register budget holds only one row's D values
+  constexpr int NR = (FM >= 2 && WGM * WGN < 16) ? 2 : 1;
   const float w2 = (TRI && ti != tj) ? 2.f : 1.f;
 #pragma clang loop unroll(full)
-  for (int fm = 0; fm < BM / WGM / 16; ++fm) {
-    float sq = 0.f;
-#pragma clang loop unroll(full)
-    for (int fn = 0; fn < BN / WGN / 16; ++fn)
-      sq += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm, fn, acc[fm][fn]);
-    if (TRI && p.sumsq != nullptr) wave_sum_store(w2 * sq, sumsq_slot<BM, WGM, WGN>(p, L, wave, fm));
+  for (int fm0 = 0; fm0 < FM; fm0 += NR) {
+    f32x4 rows[NR * FN];
+#pragma unroll
+    for (int f = 0; f < NR * FN; ++f) rows[f] = acc[fm0 + f / FN][f % FN];
+    float sq[NR];
+    epilogue_rows<BM, BN, WGM, WGN, TRI, NR>(p, bz, ti, tj, wave, fm0, rows, sq);
+    if (TRI && p.sumsq != nullptr) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) wave_sum_store(w2 * sq[k], sumsq_slot<BM, WGM, WGN>(p, L, wave, fm0 + k));
+    }
   }
 }
 
@@ -456,11 +531,10 @@ gemm_nt_kernel(const GemmParams p) {
       for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * 64] = sum[fn];
       return;
     }
-    float sq = 0.f;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) sq += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, 0, fm, fn, sum[fn]);
+    float sq[1];
+    epilogue_rows<BM, BN, WGM, WGN, TRI, 1>(p, bz, ti, tj, 0, fm, sum, sq);
     if (TRI && p.sumsq != nullptr)
-      wave_sum_store((ti != tj ? 2.f : 1.f) * sq, sumsq_slot<BM, WGM, WGN>(p, L, 0, fm));
+      wave_sum_store((ti != tj ? 2.f : 1.f) * sq[0], sumsq_slot<BM, WGM, WGN>(p, L, 0, fm));
     return;
   }
 
@@ -515,11 +589,10 @@ gemm_nt_reduce_kernel(const GemmParams p) {
   for (; sp < p.split; ++sp)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] += src[(int64_t)sp * FF + fn * 64];
-  float sq = 0.f;
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) sq += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, w, fm, fn, acc[fn]);
+  float sq[1];
+  epilogue_rows<BM, BN, WGM, WGN, TRI, 1>(p, bz, ti, tj, w, fm, acc, sq);
   if (TRI && p.sumsq != nullptr)
-    wave_sum_store((ti != tj ? 2.f : 1.f) * sq, sumsq_slot<BM, WGM, WGN>(p, p.nfull + t, w, fm));
+    wave_sum_store((ti != tj ? 2.f : 1.f) * sq[0], sumsq_slot<BM, WGM, WGN>(p, p.nfull + t, w, fm));
 }
 
 // Improved initial normalisation ("msign算子的Newton-Schulz迭代（上）"
