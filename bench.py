@@ -228,8 +228,17 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ktime = M.read_kernel_timing() if with_timing else None
+    plain_ms = None
     if with_timing:
         M.kernel_timing(False)
+        # the same steps once more with no events at all (small problems are
+        # launch-bound, and the events of the timed region show up there)
+        torch.cuda.synchronize()
+        p0 = time.perf_counter()
+        for _ in range(steps):
+            one_step()
+        torch.cuda.synchronize()
+        plain_ms = 1e3 * (time.perf_counter() - p0) / steps
 
     elapsed = t1 - t0
     nmat = sum(x.shape[0] for x in xs)
@@ -256,6 +265,8 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
         "effective_tflops": eff_tflops,
         "effective_frac_of_peak": eff_tflops / PEAK_TFLOPS[cdt],
     }
+    if plain_ms is not None:
+        rec["ms_per_step_without_events"] = plain_ms
     if ktime is not None:
         per = {}
         for k in ("normalize", "xxt", "square", "rect"):

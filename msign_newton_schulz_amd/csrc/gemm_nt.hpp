@@ -179,7 +179,11 @@ __device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] *= f;
   }
-  for (int o = 0; o < p.nout; ++o) {
+  // constant output indices (a runtime index into the by-value kernel
+  // argument would make the compiler copy the whole struct to scratch)
+#pragma unroll
+  for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
+    if (o >= p.nout) break;
     const OutSpec& os = p.out[o];
     float w[4];
 #pragma unroll
