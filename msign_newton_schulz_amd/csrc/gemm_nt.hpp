@@ -114,6 +114,41 @@ __device__ __forceinline__ int swz(int row, int ch) {
   else return ch ^ ((row >> 1) & 3);
 }
 
+// 16-byte chunk position inside a row of a K-major ("transposed") A tile,
+// [k][m] with m contiguous.  A transpose read of 16-bit data fetches, per
+// half-wave, K rows k0..k0+3 and k0+8..k0+11 (k0 a multiple of 4) x 32
+// bytes; XOR-ing the chunk pair index with bits 0, 1 and 3 of k puts those
+// 8 rows on 8 distinct 32-byte bank groups (rows of 8 chunks only allow
+// bits 0 and 1).  The fp32 reads fetch 4 groups of rows 4 apart x 64 bytes.
+// CPRA: chunks per row (at least 8 for 16-bit, 16 for fp32).
+template <int ESZ, int CPRA>
+__device__ __forceinline__ int swz_t(int k, int ch) {
+  if constexpr (ESZ == 2 && CPRA >= 16) return ch ^ (((k & 3) | ((k >> 1) & 4)) << 1);
+  else if constexpr (ESZ == 2) return ch ^ ((k & 3) << 1);
+  else return ch ^ (((k >> 2) & 3) << 2);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two LDS transpose reads (ds_read_b64_tr_b16) at byte offsets off0 and off1
+// of an LDS tile, concatenated into one 16-byte MFMA fragment.  Per 16-lane
+// group, lanes 4b .. 4b + 3 point at K row b, columns 0, 4, 8, 12; after the
+// read, lane j holds column j at K rows 0..3.
+__device__ __forceinline__ u32x4 lds_read_tr16_pair(const void* tile, int off0, int off1) {
+  const char* base = static_cast<const char*>(tile);
+  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + off0));
+  const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + off1));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+  return u32x4{w0[0], w0[1], w1[0], w1[1]};
+}
+
+// Buffer descriptor over `bytes` bytes at `base`: loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
 // L2; renumber so that every XCD works on one contiguous range of tiles.
 __device__ __forceinline__ int xcd_contiguous(int b, int nb) {
@@ -329,7 +364,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW>
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW, bool AT>
 __global__ void __launch_bounds__(WGM * WGN * KW * 64)
 gemm_nt_kernel(const GemmParams p) {
   constexpr int NT = WGM * WGN * KW * 64;
@@ -349,6 +384,12 @@ gemm_nt_kernel(const GemmParams p) {
   static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile/thread mismatch");
   static_assert(!TRI || BM == BN, "triangle mode needs square tiles");
   static_assert(NST >= 1 && NST <= 3, "one to three K slices of register prefetch");
+  // AT: P is stored K-major ([K][M], row pitch ldp): the A tile of a slice is
+  // KTE rows of BM elements (CPRA chunks each) in LDS, read back with
+  // transpose reads (16-bit) or element reads (fp32).
+  static_assert(!AT || !TRI, "transposed A only for rectangular products");
+  constexpr int CPRA = AT ? BM * ESZ / 16 : CPR;
+  static_assert(!AT || (CPRA >= (ESZ == 2 ? 8 : 16) && (KTE * CPRA * KW) % NT == 0), "transposed A tile layout");
 
   __shared__ u32x4 lds[2][KW * (BM + BN) * CPR];  // [stage][A slices, then B slices]
 
@@ -398,16 +439,49 @@ gemm_nt_kernel(const GemmParams p) {
   const int a_step = KW > 1 ? KTE * ESZ : RSTEP * (int)p.ldp * ESZ;
   const int b_step = KW > 1 ? KTE * ESZ : RSTEP * (int)p.ldq * ESZ;
   const int lds_w = row0 * CPR + swz<CPR>(row0, ch0);  // + s * RSTEP * CPR
+  // AT: chunk s * NT + tid of a slice is K row kr = (s * NT + tid) / CPRA,
+  // logical chunk tid % CPRA (NT is a multiple of CPRA), stored at its
+  // swizzled position.  Each slice gets its own descriptor starting at its
+  // first K row (column m0), so offsets stay small and reads past the
+  // matrix's last row return zeros; columns past M feed only rows of the
+  // result that are never stored.
+  const char* Pk = static_cast<const char*>(p.P) + (bz * p.sp + m0) * ESZ;
+  const int64_t pk_bytes = ((int64_t)p.K * p.ldp - m0) * ESZ;
+  // Chunk s sits NT / CPRA K rows below chunk 0 (with K-split waves, the
+  // same row of slice s); when that is a multiple of the swizzle's period in
+  // k (16) its LDS slot is chunk 0's plus s NT.
+  constexpr int AT_RSTEP = AT ? NT / CPRA : 1;
+  const int at_kr = tid / CPRA, at_c = tid % CPRA;
+  const int at_goff = (at_kr * (int)p.ldp + at_c * CE) * ESZ;
+  const int at_gstep = AT_RSTEP * (int)p.ldp * ESZ;
+  auto at_slot = [&](int s) {
+    if constexpr (AT_RSTEP % 16 == 0) {
+      return at_kr * CPRA + swz_t<ESZ, CPRA>(at_kr, at_c) + s * NT;
+    } else {
+      const int kr = at_kr + s * AT_RSTEP;
+      return kr * CPRA + swz_t<ESZ, CPRA>(kr, at_c);
+    }
+  };
 
 
   // K is a multiple of 64 elements (host contract), so every slice is whole;
   // slices past the end (the last prefetches) read past the row or past
   // num_records and are never copied into LDS.
   auto gload = [&](u32x4* dst, int k0) {
+    if constexpr (AT) {
+      const int64_t left = pk_bytes - (int64_t)k0 * p.ldp * ESZ;
+      const int64_t span = (int64_t)ACH * AT_RSTEP * p.ldp * ESZ;  // the K rows of one load step
+      const int nrec = left <= 0 ? 0 : (int)(left < span ? left : span);
+      const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Pk + (int64_t)k0 * p.ldp * ESZ, nrec);
 #pragma unroll
-    for (int s = 0; s < ACH; ++s)
-      dst[s] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, a_base + s * a_step + k0 * ESZ, 0, 0));
+      for (int s = 0; s < ACH; ++s)
+        dst[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA, at_goff + s * at_gstep, 0, 0));
+    } else {
+#pragma unroll
+      for (int s = 0; s < ACH; ++s)
+        dst[s] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rP, a_base + s * a_step + k0 * ESZ, 0, 0));
+    }
 #pragma unroll
     for (int s = 0; s < BCH; ++s)
       dst[ACH + s] = __builtin_bit_cast(
@@ -415,7 +489,13 @@ gemm_nt_kernel(const GemmParams p) {
   };
   auto lstore = [&](const u32x4* src, int buf) {
 #pragma unroll
-    for (int s = 0; s < ACH; ++s) lds[buf][lds_w + s * RSTEP * CPR] = src[s];
+    for (int s = 0; s < ACH; ++s) {
+      if constexpr (AT) {
+        lds[buf][at_slot(s)] = src[s];
+      } else {
+        lds[buf][lds_w + s * RSTEP * CPR] = src[s];
+      }
+    }
 #pragma unroll
     for (int s = 0; s < BCH; ++s) lds[buf][KW * BM * CPR + lds_w + s * RSTEP * CPR] = src[ACH + s];
   };
@@ -437,10 +517,40 @@ gemm_nt_kernel(const GemmParams p) {
     for (int kk = 0; kk < KSUB; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
       u32x4 a[FM];
+      if constexpr (AT && ESZ == 2) {
+        // K rows 32 kk + 8 g + (r / 4) and that + 4, columns m .. m + 3 of
+        // the fragment's 16: after the transpose reads lane (g, r) holds
+        // column r at K = 32 kk + 8 g + 0..7, the order of the B fragment
+        const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int row = wm * WM + fm * 16 + (lane & 15);
-        a[fm] = lds[buf][(kw * BM + row) * CPR + swz<CPR>(row, ch)];
+        for (int fm = 0; fm < FM; ++fm) {
+          const int m = wm * WM + fm * 16 + 4 * (r & 3);
+          const int k0r = kk * 32 + 8 * g + (r >> 2), k1r = k0r + 4;
+          const int off0 = k0r * CPRA * 16 + swz_t<2, CPRA>(k0r, m >> 3) * 16 + (m & 7) * 2;
+          const int off1 = k1r * CPRA * 16 + swz_t<2, CPRA>(k1r, m >> 3) * 16 + (m & 7) * 2;
+          a[fm] = lds_read_tr16_pair(&lds[buf][kw * BM * CPR], off0, off1);
+        }
+      } else if constexpr (AT) {
+        // fp32: lane (g, r) reads column r at K = 16 kk + 4 g + 0..3
+        const int g = lane >> 4, r = lane & 15;
+        const float* base = reinterpret_cast<const float*>(&lds[buf][kw * BM * CPR]);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int m = wm * WM + fm * 16 + r;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int k = kk * 16 + 4 * g + e;
+            v[e] = base[k * CPRA * 4 + swz_t<4, CPRA>(k, m >> 2) * 4 + (m & 3)];
+          }
+          a[fm] = __builtin_bit_cast(u32x4, v);
+        }
+      } else {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int row = wm * WM + fm * 16 + (lane & 15);
+          a[fm] = lds[buf][(kw * BM + row) * CPR + swz<CPR>(row, ch)];
+        }
       }
       if constexpr (kAllFrags) {
         u32x4 b[FN];

@@ -95,7 +95,7 @@ struct Carver {
 struct NsPlan {
   Shape s;
   int32_t nblk;
-  size_t x32t[2], xh[2], xht[2], a, b, partial, sumsq, scales, split, split_bytes, total;
+  size_t x32[2], xh[2], a, b, partial, sumsq, scales, split, split_bytes, total;
 };
 
 NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
@@ -106,9 +106,8 @@ NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
   const size_t nm = (size_t)batch * p.s.np * p.s.mp, nn = (size_t)batch * p.s.np * p.s.np;
   Carver c;
   for (int i = 0; i < 2; ++i) {
-    p.x32t[i] = c.take(nm * 4);
+    p.x32[i] = c.take(nm * 4);
     p.xh[i] = c.take(nm * cs);
-    p.xht[i] = c.take(nm * cs);
   }
   p.a = c.take(nn * cs);
   p.b = c.take(nn * cs);
@@ -124,7 +123,7 @@ NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
 struct GramPlan {
   Shape s;
   int32_t nblk;
-  size_t xh[2], xht[2], r, z, rz, q[2], partial, split, split_bytes, total;
+  size_t xh[2], r, z, rz, q[2], partial, split, split_bytes, total;
 };
 
 GramPlan plan_gram(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
@@ -136,7 +135,6 @@ GramPlan plan_gram(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
   Carver c;
   for (int i = 0; i < 2; ++i) {
     p.xh[i] = c.take(nm * cs);
-    p.xht[i] = c.take(nm * cs);
   }
   p.r = c.take(nn * cs);
   p.z = c.take(nn * cs);
@@ -274,7 +272,7 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   return l;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW>
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW, bool AT>
 hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
   q.tiles_m = l.tiles_m;
   q.tiles_n = l.tiles_n;
@@ -283,7 +281,8 @@ hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
   q.split = l.split;
   const int64_t blocks = l.nfull + l.tail * l.split;
   if (blocks == 0) return hipSuccess;
-  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI, KW><<<dim3((unsigned)blocks), WGM * WGN * KW * 64, 0, st>>>(q);
+  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI, KW, AT>
+      <<<dim3((unsigned)blocks), WGM * WGN * KW * 64, 0, st>>>(q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || l.tail == 0) return e;
   gemm_nt_reduce_kernel<T, BM, BN, WGM, WGN, TRI>
@@ -293,15 +292,24 @@ hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
 
 template <typename T, bool TRI>
 hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
-  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 1, TRI, 1>(q, l, st);
-  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI, 1>(q, l, st);
-  return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI, 4>(q, l, st);
+  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 1, TRI, 1, false>(q, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI, 1, false>(q, l, st);
+  return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI, 4, false>(q, l, st);
+}
+
+// Rectangular products with P stored K-major (the iterate X, n x m, read
+// as X^T).
+template <typename T>
+hipError_t launch_nt_at(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
+  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 1, false, 1, true>(q, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, false, 1, true>(q, l, st);
+  return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, true>(q, l, st);
 }
 
 // Launch one product.  `partial`/`partial_cap` is workspace for the K-split
 // tail; with too little of it the tail is computed whole instead.
 hipError_t launch_nt(int32_t cdt, bool tri, GemmParams q, int64_t batch, hipStream_t st,
-                     void* partial = nullptr, size_t partial_cap = 0) {
+                     void* partial = nullptr, size_t partial_cap = 0, bool at = false) {
   LaunchPlan l = plan_launch(q.M, q.N, q.K, batch, tri, cdt);
   if (l.tail > 0 && (partial == nullptr || partial_cap < l.partial_bytes)) {
     l.nfull = l.nt;
@@ -309,6 +317,13 @@ hipError_t launch_nt(int32_t cdt, bool tri, GemmParams q, int64_t batch, hipStre
     l.split = 1;
   }
   q.partial = static_cast<float*>(partial);
+  if (at) {
+    switch (cdt) {
+      case MSIGN_BF16: return launch_nt_at<bf16_t>(q, l, st);
+      case MSIGN_F16: return launch_nt_at<f16_t>(q, l, st);
+      default: return launch_nt_at<float>(q, l, st);
+    }
+  }
   switch (cdt) {
     case MSIGN_BF16: return tri ? launch_nt_t<bf16_t, true>(q, l, st) : launch_nt_t<bf16_t, false>(q, l, st);
     case MSIGN_F16: return tri ? launch_nt_t<f16_t, true>(q, l, st) : launch_nt_t<f16_t, false>(q, l, st);
@@ -329,7 +344,7 @@ size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt) {
   size_t b = 0;
   const LaunchPlan ls[3] = {plan_launch(s.np, s.np, s.mp, batch, true, cdt),
                             plan_launch(s.np, s.np, s.np, batch, true, cdt),
-                            plan_launch(s.np, s.mp, s.np, batch, false, cdt)};
+                            plan_launch(s.mp, s.np, s.np, batch, false, cdt)};
   for (const LaunchPlan& l : ls) b = l.partial_bytes > b ? l.partial_bytes : b;
   return b;
 }
@@ -455,12 +470,13 @@ void coeff_at(const float* coeffs, int t, float* a, float* b, float* c) {
   *a = r[0]; *b = r[1]; *c = r[2];
 }
 
-// Final output y (io dtype, user layout): C is n x m; wide -> y[i][j],
-// tall -> y[j][i] (y is m x n).
+// Final output y (io dtype, user layout) of a product C' = X^T Z (m x n, C'
+// [i][j] = X'[j][i]): wide -> y[j][i] (y is n x m, a transposed store),
+// tall -> y[i][j] (y is m x n).
 void add_final_out(GemmParams& g, void* y, const Shape& s, int32_t io_dtype) {
   const int64_t ld = s.tall ? s.n : s.m;
-  const bool vec = s.tall && (s.n % 4 == 0) && aligned(y, 4 * dt_size(io_dtype));
-  add_out(g, y, ld, s.n * s.m, io_dtype, s.tall, s.n, s.m, 0.f, 0, vec);
+  const bool vec = !s.tall && (s.m % 4 == 0) && aligned(y, 4 * dt_size(io_dtype));
+  add_out(g, y, ld, s.n * s.m, io_dtype, !s.tall, s.m, s.n, 0.f, 0, vec);
 }
 
 }  // namespace
@@ -508,9 +524,8 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
   const Shape& s = pl.s;
   const int32_t cdt = compute_dtype;
   const int64_t nm = s.np * s.mp, nn = s.np * s.np;
-  void* x32t[2] = {at(workspace, pl.x32t[0]), at(workspace, pl.x32t[1])};
+  void* x32[2] = {at(workspace, pl.x32[0]), at(workspace, pl.x32[1])};
   void* xh[2] = {at(workspace, pl.xh[0]), at(workspace, pl.xh[1])};
-  void* xht[2] = {at(workspace, pl.xht[0]), at(workspace, pl.xht[1])};
   void* A = at(workspace, pl.a);
   void* B = at(workspace, pl.b);
   float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
@@ -518,13 +533,13 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
   float* scales = reinterpret_cast<float*>(at(workspace, pl.scales));
   void* split = at(workspace, pl.split);
 
-  // X0: Xh (n x m), Xht and X32t (m x n, i.e. transposed relative to X)
-  NormOut outs[3] = {
+  // X0 (n x m): in the compute dtype (the X X^T operand, also read K-major
+  // as X^T by the update) and the fp32 master
+  NormOut outs[2] = {
       {xh[0], s.mp, nm, cdt, 0},
-      {xht[0], s.np, nm, cdt, 1},
-      {x32t[0], s.np, nm, MSIGN_F32, 1},
+      {x32[0], s.mp, nm, MSIGN_F32, 0},
   };
-  st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 3, stream);
+  st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 2, stream);
   if (st != MSIGN_OK) return st;
 
   for (int t = 0; t < steps; ++t) {
@@ -576,20 +591,20 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
       e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "c A A + b A");
     }
-    {  // X' = B X + a X
-      GemmParams g = gemm_base(cubic ? A : B, s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np,
+    {  // X' = B X + a X, as C' = X^T B + a X^T (m x n) with X read K-major;
+       // C'[i][j] is stored at X'[j][i], four consecutive i per store
+      GemmParams g = gemm_base(xh[cur], s.mp, nm, cubic ? A : B, s.np, nn, s.mp, s.np, s.np,
                                cubic ? b : 1.f);
       if (rescale) g.vscale = scales;
-      set_d(g, x32t[cur], s.np, nm, MSIGN_F32, a, true);
+      set_d(g, x32[cur], s.mp, nm, MSIGN_F32, a, true);
       if (t + 1 < steps) {
-        add_out(g, x32t[nxt], s.np, nm, MSIGN_F32, true, s.np, s.mp, 0.f, 0, true);
-        add_out(g, xh[nxt], s.mp, nm, cdt, false, s.np, s.mp, 0.f, 0, false);
-        add_out(g, xht[nxt], s.np, nm, cdt, true, s.np, s.mp, 0.f, 0, true);
+        add_out(g, x32[nxt], s.mp, nm, MSIGN_F32, true, s.mp, s.np, 0.f, 0, true);
+        add_out(g, xh[nxt], s.mp, nm, cdt, true, s.mp, s.np, 0.f, 0, true);
       } else {
         add_final_out(g, y, s, io_dtype);
       }
       TimedLaunch tl(KC_RECT, stream);
-      e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes);
+      e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes, true);
       if (e != hipSuccess) return hip_fail(e, "B X + a X");
     }
   }
@@ -626,7 +641,6 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
   const int32_t cdt = compute_dtype;
   const int64_t nm = s.np * s.mp, nn = s.np * s.np;
   void* xh[2] = {at(workspace, pl.xh[0]), at(workspace, pl.xh[1])};
-  void* xht[2] = {at(workspace, pl.xht[0]), at(workspace, pl.xht[1])};
   void* R = at(workspace, pl.r);
   void* Z = at(workspace, pl.z);
   void* RZ = at(workspace, pl.rz);
@@ -634,8 +648,8 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
   float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
   void* split = at(workspace, pl.split);
 
-  NormOut outs[2] = {{xh[0], s.mp, nm, cdt, 0}, {xht[0], s.np, nm, cdt, 1}};
-  st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 2, stream);
+  NormOut outs[1] = {{xh[0], s.mp, nm, cdt, 0}};
+  st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 1, stream);
   if (st != MSIGN_OK) return st;
 
   hipError_t e;
@@ -682,12 +696,12 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
       if (st != MSIGN_OK) return st;
     }
     if (restart_at[t]) {  // X <- Q X, R = X X^T, Q = I
-      GemmParams g = gemm_base(Qb[qc], s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np, 1.f);
-      add_out(g, xh[cur ^ 1], s.mp, nm, cdt, false, s.np, s.mp, 0.f, 0, false);
-      add_out(g, xht[cur ^ 1], s.np, nm, cdt, true, s.np, s.mp, 0.f, 0, true);
+      // as C' = X^T Q (Q symmetric), stored transposed into the other X
+      GemmParams g = gemm_base(xh[cur], s.mp, nm, Qb[qc], s.np, nn, s.mp, s.np, s.np, 1.f);
+      add_out(g, xh[cur ^ 1], s.mp, nm, cdt, true, s.mp, s.np, 0.f, 0, true);
       {
         TimedLaunch tl(KC_RECT, stream);
-        e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes);
+        e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes, true);
         if (e != hipSuccess) return hip_fail(e, "restart X <- Q X");
       }
       cur ^= 1;
@@ -697,10 +711,10 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     }
   }
   {  // y = Q X
-    GemmParams g = gemm_base(Qb[qc], s.np, nn, xht[cur], s.np, nm, s.np, s.mp, s.np, 1.f);
+    GemmParams g = gemm_base(xh[cur], s.mp, nm, Qb[qc], s.np, nn, s.mp, s.np, s.np, 1.f);
     add_final_out(g, y, s, io_dtype);
     TimedLaunch tl(KC_RECT, stream);
-    e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes);
+    e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes, true);
     if (e != hipSuccess) return hip_fail(e, "y = Q X");
   }
   return MSIGN_OK;
