@@ -347,8 +347,9 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
                                          int wave) {
   constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
   // fragment rows whose D loads share a round trip: two, except in the
-  // 16-wave tile, whose 128-register budget holds only one row's D values
-  constexpr int NR = (FM >= 2 && WGM * WGN < 16) ? 2 : 1;
+  // 16-wave rectangular tile, whose 128-register budget (next to its
+  // K-major A addressing) holds only one row's D values without spilling
+  constexpr int NR = (FM >= 2 && (WGM * WGN < 16 || TRI)) ? 2 : 1;
   const float w2 = (TRI && ti != tj) ? 2.f : 1.f;
 #pragma clang loop unroll(full)
   for (int fm0 = 0; fm0 < FM; fm0 += NR) {
