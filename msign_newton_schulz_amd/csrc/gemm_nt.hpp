@@ -341,11 +341,94 @@ __device__ __forceinline__ float* sumsq_slot(const GemmParams& p, int L, int wav
   return p.sumsq + ((int64_t)L * (WGM * WGN) + wave) * (BM / WGM / 16) + fm;
 }
 
+// Epilogue of a rectangular tile whose outputs are all stored transposed
+// (C[i][j] at ptr[j ld + i]) with 4-wide stores and lie wholly in bounds.
+// The MFMA lane layout gives each store instruction 16 rows j x 4 values:
+// partial cache lines.  Instead each wave stages one 16-column group (16 j
+// x its 64 i) at a time in its own LDS region (rows padded to 68 floats:
+// conflict-free 16-byte writes and reads) and reads it back by rows, so 16
+// lanes store one row's 64 consecutive i (256 bytes fp32, 128 bytes 16-bit)
+// per instruction.  Returns false, having done nothing, when the tile does
+// not qualify.  The LDS ring must be free (after the K loop's last barrier).
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz, int ti, int tj,
+                                                const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
+                                                int wave, float* stage) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  constexpr int PITCH = 68;
+  static_assert(WM == 64, "16 lanes x 4 values cover a row of the wave tile");
+  const int m0 = ti * BM, n0 = tj * BN;
+  if (p.nout < 1) return false;
+#pragma unroll
+  for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
+    if (o >= p.nout) break;
+    const OutSpec& os = p.out[o];
+    if (!os.transposed || !os.vec_ok || os.diag_lim > 0 || m0 + BM > os.rows_lim || n0 + BN > os.cols_lim)
+      return false;
+  }
+  const bool has_d = p.Dt != nullptr;
+  if (has_d && !(p.d_vec_ok && m0 + BM <= p.M && n0 + BN <= p.N)) return false;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wm = wave / WGN, wn = wave % WGN;
+  float* st = stage + wave * (16 * PITCH);
+  const float f = p.vscale != nullptr ? p.vscale[4 * bz] : 1.f;
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int jf = n0 + wn * WN + fn * 16;  // first j of the group
+    float d[FM][4];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[fm][r] = 0.f;
+    if (has_d) {
+      const int64_t base = bz * p.sd + (int64_t)(jf + c) * p.ldd + m0 + wm * WM + 4 * g;
+      if (p.d_dtype == DT_F32) {
+        f32x4 t[FM];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          t[fm] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.Dt) + base + fm * 16);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d[fm][r] = t[fm][r];
+      } else {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) load_vec4(p.Dt, base + fm * 16, p.d_dtype, d[fm]);
+      }
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      f32x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (p.alpha * acc[fm][fn][r] + p.beta * d[fm][r]) * f;
+      *reinterpret_cast<f32x4*>(st + c * PITCH + fm * 16 + 4 * g) = v;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 4 * q + g;
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c);
+      const float w[4] = {w4[0], w4[1], w4[2], w4[3]};
+      const int j = jf + row;
+      const int i = m0 + wm * WM + 4 * c;
+#pragma unroll
+      for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
+        if (o >= p.nout) break;
+        const OutSpec& os = p.out[o];
+        store_vec4(os.ptr, bz * os.bstride + (int64_t)j * os.ld + i, os.dtype, w);
+      }
+    }
+  }
+  return true;
+}
+
 template <int BM, int BN, int WGM, int WGN, bool TRI>
 __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz, int ti, int tj,
                                          const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
-                                         int wave) {
+                                         int wave, float* stage = nullptr) {
   constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
+  if constexpr (!TRI && BM / WGM == 64) {
+    if (stage != nullptr && epilogue_staged<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) return;
+  }
   // fragment rows whose D loads share a round trip: two, except in the
   // 16-wave rectangular tile, whose 128-register budget (next to its
   // K-major A addressing) holds only one row's D values without spilling
@@ -665,7 +748,9 @@ gemm_nt_kernel(const GemmParams p) {
       for (int fn = 0; fn < FN; ++fn) dst[(fm * FN + fn) * 64] = acc[fm][fn];
     return;
   }
-  epilogue<BM, BN, WGM, WGN, TRI>(p, L, bz, ti, tj, acc, wave);
+  // (the last K iteration ended with a barrier: the LDS ring is free)
+  static_assert(KW > 1 || WGM * WGN * 16 * 68 * 4 <= (int)sizeof(lds), "staging fits the LDS ring");
+  epilogue<BM, BN, WGM, WGN, TRI>(p, L, bz, ti, tj, acc, wave, reinterpret_cast<float*>(&lds[0][0]));
 }
 
 // Second pass for split tiles.  Block (t, w) takes wave w's fragments of
