@@ -421,6 +421,85 @@ __device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz,
   return true;
 }
 
+// Same for an off-diagonal tile of a triangle product, which is stored
+// twice: C[i][j] at ptr[i ld + j] and its mirror at ptr[j ld + i].  Two
+// passes through the wave's LDS region: 16-column groups read back by rows
+// give the mirror stores, 16-row groups read back by rows the direct ones.
+// D (symmetric, as every D of a triangle product is) is added after the
+// read-back, loaded by rows too.  Diagonal tiles (masking, diagonal terms)
+// return false.
+template <int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ bool epilogue_staged_tri(const GemmParams& p, int64_t bz, int ti, int tj,
+                                                    const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
+                                                    int wave, float* stage) {
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  constexpr int PITCH = 68;
+  static_assert(WM == 64 && WN == 64, "16 lanes x 4 values cover a row of the wave tile");
+  if (ti == tj || p.nout < 1) return false;
+  const int m0 = ti * BM, n0 = tj * BN;
+#pragma unroll
+  for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
+    if (o >= p.nout) break;
+    const OutSpec& os = p.out[o];
+    if (!os.vec_ok || m0 + BM > os.rows_lim || n0 + BN > os.cols_lim || n0 + BN > os.rows_lim ||
+        m0 + BM > os.cols_lim)
+      return false;
+  }
+  const bool has_d = p.Dt != nullptr;
+  if (has_d && !(p.d_vec_ok && m0 + BM <= p.M && n0 + BN <= p.N)) return false;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int ib = m0 + wm * WM, jb = n0 + wn * WN;  // first row and column of the wave tile
+  float* st = stage + wave * (16 * PITCH);
+  // finish four consecutive values of C along `along` at (r0, c0..c0+3),
+  // where D[r][c] = Dt[r ldd + c] by symmetry, and store them at
+  // ptr[r0 ld + c0] of every output
+  auto finish = [&](const f32x4& a, int r0, int c0) {
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    if (has_d) load_vec4(p.Dt, bz * p.sd + (int64_t)r0 * p.ldd + c0, p.d_dtype, d);
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = p.alpha * a[r] + p.beta * d[r];
+    if (p.vscale != nullptr) {
+      const float f = p.vscale[4 * bz];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] *= f;
+    }
+#pragma unroll
+    for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
+      if (o >= p.nout) break;
+      const OutSpec& os = p.out[o];
+      store_vec4(os.ptr, bz * os.bstride + (int64_t)r0 * os.ld + c0, os.dtype, w);
+    }
+  };
+  // mirror: column group fn staged as [j][i], rows j stored at ptr[j ld + i]
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      *reinterpret_cast<f32x4*>(st + c * PITCH + fm * 16 + 4 * g) = acc[fm][fn];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 4 * q + g;
+      finish(*reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c), jb + fn * 16 + row, ib + 4 * c);
+    }
+  }
+  // direct: row group fm staged as [i][j], rows i stored at ptr[i ld + j]
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[(4 * g + r) * PITCH + fn * 16 + c] = acc[fm][fn][r];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 4 * q + g;
+      finish(*reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c), ib + fm * 16 + row, jb + 4 * c);
+    }
+  }
+  return true;
+}
+
 template <int BM, int BN, int WGM, int WGN, bool TRI>
 __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz, int ti, int tj,
                                          const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
@@ -428,6 +507,22 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
   constexpr int FM = BM / WGM / 16, FN = BN / WGN / 16;
   if constexpr (!TRI && BM / WGM == 64) {
     if (stage != nullptr && epilogue_staged<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) return;
+  }
+  if constexpr (TRI && BM / WGM == 64 && BN / WGN == 64) {
+    if (stage != nullptr && epilogue_staged_tri<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) {
+      if (p.sumsq != nullptr) {  // acc^2 sums per fragment row, off-diagonal: counted twice
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          float sq = 0.f;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sq += acc[fm][fn][r] * acc[fm][fn][r];
+          wave_sum_store(2.f * sq, sumsq_slot<BM, WGM, WGN>(p, L, wave, fm));
+        }
+      }
+      return;
+    }
   }
   // fragment rows whose D loads share a round trip: two, except in the
   // 16-wave rectangular tile, whose 128-register budget (next to its
