@@ -292,6 +292,7 @@ hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
 
 template <typename T, bool TRI>
 hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
+  static_assert(TRI, "rectangular products go through launch_nt_at");
   if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 1, TRI, 1, false>(q, l, st);
   if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI, 1, false>(q, l, st);
   return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI, 4, false>(q, l, st);
@@ -306,10 +307,15 @@ hipError_t launch_nt_at(const GemmParams& q, const LaunchPlan& l, hipStream_t st
   return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, true>(q, l, st);
 }
 
-// Launch one product.  `partial`/`partial_cap` is workspace for the K-split
-// tail; with too little of it the tail is computed whole instead.
-hipError_t launch_nt(int32_t cdt, bool tri, GemmParams q, int64_t batch, hipStream_t st,
-                     void* partial = nullptr, size_t partial_cap = 0, bool at = false) {
+// Launch one product: a triangle product (both operands read along K, P == Q
+// symmetric or P Q^T symmetric) or a rectangular one with P stored K-major.
+// `partial`/`partial_cap` is workspace for the K-split tail; with too little
+// of it the tail is computed whole instead.
+enum ProductKind { TRIANGLE, RECT_KMAJOR };
+
+hipError_t launch_nt(int32_t cdt, ProductKind kind, GemmParams q, int64_t batch, hipStream_t st,
+                     void* partial = nullptr, size_t partial_cap = 0) {
+  const bool tri = kind == TRIANGLE;
   LaunchPlan l = plan_launch(q.M, q.N, q.K, batch, tri, cdt);
   if (l.tail > 0 && (partial == nullptr || partial_cap < l.partial_bytes)) {
     l.nfull = l.nt;
@@ -317,17 +323,10 @@ hipError_t launch_nt(int32_t cdt, bool tri, GemmParams q, int64_t batch, hipStre
     l.split = 1;
   }
   q.partial = static_cast<float*>(partial);
-  if (at) {
-    switch (cdt) {
-      case MSIGN_BF16: return launch_nt_at<bf16_t>(q, l, st);
-      case MSIGN_F16: return launch_nt_at<f16_t>(q, l, st);
-      default: return launch_nt_at<float>(q, l, st);
-    }
-  }
   switch (cdt) {
-    case MSIGN_BF16: return tri ? launch_nt_t<bf16_t, true>(q, l, st) : launch_nt_t<bf16_t, false>(q, l, st);
-    case MSIGN_F16: return tri ? launch_nt_t<f16_t, true>(q, l, st) : launch_nt_t<f16_t, false>(q, l, st);
-    default: return tri ? launch_nt_t<float, true>(q, l, st) : launch_nt_t<float, false>(q, l, st);
+    case MSIGN_BF16: return tri ? launch_nt_t<bf16_t, true>(q, l, st) : launch_nt_at<bf16_t>(q, l, st);
+    case MSIGN_F16: return tri ? launch_nt_t<f16_t, true>(q, l, st) : launch_nt_at<f16_t>(q, l, st);
+    default: return tri ? launch_nt_t<float, true>(q, l, st) : launch_nt_at<float>(q, l, st);
   }
 }
 
@@ -551,7 +550,7 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
       GemmParams g = gemm_base(xh[cur], s.mp, nm, xh[cur], s.mp, nm, s.np, s.np, s.mp, 1.f);
       add_out(g, A, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
       TimedLaunch tl(KC_SYRK, stream);
-      e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
+      e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "X X^T");
     }
     // Improved initial normalisation (§改良初值), first step only: A2 = A A
@@ -564,7 +563,7 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
       g.sumsq = sumsq;
       {
         TimedLaunch tl(KC_SQUARE, stream);
-        e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
+        e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
         if (e != hipSuccess) return hip_fail(e, "A A (first step)");
       }
       const LaunchPlan l = plan_launch(s.np, s.np, s.np, batch, true, cdt);
@@ -588,7 +587,7 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
       set_d(g, A, s.np, nn, cdt, b, true);
       add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
       TimedLaunch tl(KC_SQUARE, stream);
-      e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
+      e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "c A A + b A");
     }
     {  // X' = B X + a X, as C' = X^T B + a X^T (m x n) with X read K-major;
@@ -604,7 +603,7 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
         add_final_out(g, y, s, io_dtype);
       }
       TimedLaunch tl(KC_RECT, stream);
-      e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes, true);
+      e = launch_nt(cdt, RECT_KMAJOR, g, batch, stream, split, pl.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "B X + a X");
     }
   }
@@ -658,7 +657,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     GemmParams g = gemm_base(xh[cur], s.mp, nm, xh[cur], s.mp, nm, s.np, s.np, s.mp, 1.f);
     add_out(g, R, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
     TimedLaunch tl(KC_SYRK, stream);
-    e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
+    e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
     return e == hipSuccess ? MSIGN_OK : hip_fail(e, "R = X X^T");
   };
   // tri product: out = P Q^T + beta D  (all n x n, symmetric)
@@ -669,7 +668,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     add_out(g, out, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
     if (out2) add_out(g, out2, s.np, nn, cdt, false, s.np, s.np, diag2, s.n, true);
     TimedLaunch tl(KC_SQUARE, stream);
-    e = launch_nt(cdt, true, g, batch, stream, split, pl.split_bytes);
+    e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
     return e == hipSuccess ? MSIGN_OK : hip_fail(e, what);
   };
 
@@ -701,7 +700,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
       add_out(g, xh[cur ^ 1], s.mp, nm, cdt, true, s.mp, s.np, 0.f, 0, true);
       {
         TimedLaunch tl(KC_RECT, stream);
-        e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes, true);
+        e = launch_nt(cdt, RECT_KMAJOR, g, batch, stream, split, pl.split_bytes);
         if (e != hipSuccess) return hip_fail(e, "restart X <- Q X");
       }
       cur ^= 1;
@@ -714,7 +713,7 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     GemmParams g = gemm_base(xh[cur], s.mp, nm, Qb[qc], s.np, nn, s.mp, s.np, s.np, 1.f);
     add_final_out(g, y, s, io_dtype);
     TimedLaunch tl(KC_RECT, stream);
-    e = launch_nt(cdt, false, g, batch, stream, split, pl.split_bytes, true);
+    e = launch_nt(cdt, RECT_KMAJOR, g, batch, stream, split, pl.split_bytes);
     if (e != hipSuccess) return hip_fail(e, "y = Q X");
   }
   return MSIGN_OK;
@@ -809,7 +808,7 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_
   if (d && beta != 0.f) set_d(g, d, n, n * n, dtype, beta, (n % 4 == 0) && aligned(d, 4 * es));
   add_out(g, c, n, n * n, dtype, false, n, n, gamma, n, vec_c);
   TimedLaunch tl(KC_SYRK, stream);
-  hipError_t e = launch_nt(dtype, true, g, batch, stream, split, split_cap);
+  hipError_t e = launch_nt(dtype, TRIANGLE, g, batch, stream, split, split_cap);
   if (e != hipSuccess) return hip_fail(e, "syrk_xxt");
   return MSIGN_OK;
 }
