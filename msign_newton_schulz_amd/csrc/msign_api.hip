@@ -241,7 +241,18 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   };
   // the largest tile that still gives every CU a tile; 64 x 64 tiles (one
   // wave) when even 128 x 128 tiles leave CUs idle
-  l.bm = tiles_at(256) >= kCUs ? 256 : (tiles_at(128) >= kCUs ? 128 : 64);
+  const int64_t kslices = K / (cdt == MSIGN_F32 ? 16 : 32);
+  const int64_t t256 = tiles_at(256);
+  bool big = t256 >= kCUs;
+  if (!big && t256 > 0 && K >= 2048) {
+    // long K: a K split of the big tiles that fills most CUs beats smaller
+    // tiles (which would leave some CUs with two long tiles)
+    int64_t sp = kCUs / t256;
+    if (sp > kSplitMax) sp = kSplitMax;
+    if (sp > kslices / 4) sp = kslices / 4;
+    big = t256 * sp >= kCUs * 3 / 4;
+  }
+  l.bm = big ? 256 : (tiles_at(128) >= kCUs ? 128 : 64);
   // Blocks per CU that splitting the last round aims for (measured): one
   // 16-wave block of 256 x 256 keeps a CU busy; 4-wave 128 x 128 blocks
   // gain from two per CU.  A 64 x 64 tile is already shared along K by its
@@ -257,7 +268,6 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
   l.split = 1;
   const int64_t slots = (int64_t)kCUs * per_cu;
   const int64_t rem = l.nt % slots;
-  const int64_t kslices = K / (cdt == MSIGN_F32 ? 16 : 32);
   if (rem > 0) {
     int64_t sp = slots / rem;
     if (sp > kSplitMax) sp = kSplitMax;     // bounds the partial-sum traffic
