@@ -129,6 +129,7 @@ __device__ __forceinline__ int swz_t(int k, int ch) {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define MSIGN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Two LDS transpose reads (ds_read_b64_tr_b16) at byte offsets off0 and off1
 // of an LDS tile, concatenated into one 16-byte MFMA fragment.  Per 16-lane
@@ -562,7 +563,9 @@ gemm_nt_kernel(const GemmParams p) {
   static_assert(KW == 1 || (WGM == 1 && WGN == 1 && BM == BN && NT / CPR == BM), "K-split waves");
   static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile/thread mismatch");
   static_assert(!TRI || BM == BN, "triangle mode needs square tiles");
-  static_assert(NST >= 1 && NST <= 3, "one to three K slices of register prefetch");
+  // NST: K slices of register prefetch (1..3), or 0 for direct global->LDS
+  // loads (buffer_load ... lds) into a 2-stage ring
+  static_assert(NST >= 0 && NST <= 3 && (NST > 0 || KW == 1), "prefetch depth");
   // AT: P is stored K-major ([K][M], row pitch ldp): the A tile of a slice is
   // KTE rows of BM elements (CPRA chunks each) in LDS, read back with
   // transpose reads (16-bit) or element reads (fp32).
@@ -767,6 +770,52 @@ gemm_nt_kernel(const GemmParams p) {
     kt0 = (int)((int64_t)part * KT / p.split);
     nk = (int)((int64_t)(part + 1) * KT / p.split) - kt0;
   }
+  if constexpr (NST == 0) {
+    // Direct loads: a wave's load instruction s writes the 64 consecutive
+    // LDS slots s * NT + 64 wave + lane, i.e. row (or K row) row0 + s RSTEP,
+    // physical chunk tid % CPR (CPRA); the lane fetches the logical chunk
+    // that the swizzle puts there (an involution, the same for every s).
+    // Slice j + 1 loads into the other stage while slice j is computed; a
+    // wave waits for its own loads (vmcnt) and reads (lgkmcnt) before each
+    // barrier, so after it slice j + 1 is whole and stage j is free.
+    const int uw = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS destinations
+    int dma_a = 0;
+    if constexpr (AT) dma_a = (at_kr * (int)p.ldp + swz_t<ESZ, CPRA>(at_kr, at_c) * CE) * ESZ;
+    else dma_a = (row0 * (int)p.ldp + swz<CPR>(row0, ch0) * CE) * ESZ;
+    const int dma_b = (row0 * (int)p.ldq + swz<CPR>(row0, ch0) * CE) * ESZ;
+    auto issue = [&](int buf, int k0) {
+      if constexpr (AT) {
+        const int64_t left = pk_bytes - (int64_t)k0 * p.ldp * ESZ;
+        const int64_t span = (int64_t)ACH * AT_RSTEP * p.ldp * ESZ;
+        const int nrec = left <= 0 ? 0 : (int)(left < span ? left : span);
+        const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Pk + (int64_t)k0 * p.ldp * ESZ, nrec);
+#pragma unroll
+        for (int s = 0; s < ACH; ++s) {
+          const int off = dma_a + s * at_gstep;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MSIGN_LDS(&lds[buf][s * NT + uw * 64]), 16, off, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < ACH; ++s) {
+          const int off = dma_a + s * a_step + k0 * ESZ;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, MSIGN_LDS(&lds[buf][s * NT + uw * 64]), 16, off, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < BCH; ++s) {
+        const int off = dma_b + s * b_step + k0 * ESZ;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, MSIGN_LDS(&lds[buf][BM * CPR + s * NT + uw * 64]), 16, off,
+                                                 0, 0, 0);
+      }
+    };
+    if (nk > 0) issue(0, kt0 * KTE);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int j = 0; j < nk; ++j) {
+      if (j + 1 < nk) issue((j + 1) & 1, (kt0 + j + 1) * KTE);
+      compute(j & 1);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  } else {
   // steps of KW slices; wave kw computes slice j * KW + kw of step j when
   // that slice is in range
   const int ns = (nk + KW - 1) / KW;
@@ -795,6 +844,7 @@ gemm_nt_kernel(const GemmParams p) {
   if (j < ns) iter(j, I0{});
   if constexpr (NST >= 3) {
     if (j + 1 < ns) iter(j + 1, I1{});
+  }
   }
 
   if constexpr (KW > 1) {
