@@ -693,7 +693,7 @@ gemm_nt_kernel(const GemmParams p) {
   // 128 x 128 wave tile holds its A fragments and streams B fragments one at
   // a time to stay within the register file next to 256 accumulators.
   constexpr bool kAllFrags = (FM + FN) <= 12;
-  auto compute = [&](int buf) {
+  auto compute = [&](const u32x4* stage) {
     __builtin_amdgcn_s_setprio(1);  // favour waves that are issuing MFMAs
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
@@ -710,12 +710,12 @@ gemm_nt_kernel(const GemmParams p) {
           const int k0r = kk * 32 + 8 * g + (r >> 2), k1r = k0r + 4;
           const int off0 = k0r * CPRA * 16 + swz_t<2, CPRA>(k0r, m >> 3) * 16 + (m & 7) * 2;
           const int off1 = k1r * CPRA * 16 + swz_t<2, CPRA>(k1r, m >> 3) * 16 + (m & 7) * 2;
-          a[fm] = lds_read_tr16_pair(&lds[buf][kw * BM * CPR], off0, off1);
+          a[fm] = lds_read_tr16_pair(stage + kw * BM * CPR, off0, off1);
         }
       } else if constexpr (AT) {
         // fp32: lane (g, r) reads column r at K = 16 kk + 4 g + 0..3
         const int g = lane >> 4, r = lane & 15;
-        const float* base = reinterpret_cast<const float*>(&lds[buf][kw * BM * CPR]);
+        const float* base = reinterpret_cast<const float*>(stage + kw * BM * CPR);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
           const int m = wm * WM + fm * 16 + r;
@@ -731,7 +731,7 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
           const int row = wm * WM + fm * 16 + (lane & 15);
-          a[fm] = lds[buf][(kw * BM + row) * CPR + swz<CPR>(row, ch)];
+          a[fm] = stage[(kw * BM + row) * CPR + swz<CPR>(row, ch)];
         }
       }
       if constexpr (kAllFrags) {
@@ -739,7 +739,7 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int row = wn * WN + fn * 16 + (lane & 15);
-          b[fn] = lds[buf][(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
+          b[fn] = stage[(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -749,7 +749,7 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int row = wn * WN + fn * 16 + (lane & 15);
-          const u32x4 b = lds[buf][(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
+          const u32x4 b = stage[(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm) Mma<T>::run(acc[fm][fn], a[fm], b);
         }
@@ -783,7 +783,7 @@ gemm_nt_kernel(const GemmParams p) {
     if constexpr (AT) dma_a = (at_kr * (int)p.ldp + swz_t<ESZ, CPRA>(at_kr, at_c) * CE) * ESZ;
     else dma_a = (row0 * (int)p.ldp + swz<CPR>(row0, ch0) * CE) * ESZ;
     const int dma_b = (row0 * (int)p.ldq + swz<CPR>(row0, ch0) * CE) * ESZ;
-    auto issue = [&](int buf, int k0) {
+    auto issue = [&](u32x4* stage, int k0) {
       if constexpr (AT) {
         const int64_t left = pk_bytes - (int64_t)k0 * p.ldp * ESZ;
         const int64_t span = (int64_t)ACH * AT_RSTEP * p.ldp * ESZ;
@@ -792,27 +792,32 @@ gemm_nt_kernel(const GemmParams p) {
 #pragma unroll
         for (int s = 0; s < ACH; ++s) {
           const int off = dma_a + s * at_gstep;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MSIGN_LDS(&lds[buf][s * NT + uw * 64]), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, MSIGN_LDS(stage + s * NT + uw * 64), 16, off, 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int s = 0; s < ACH; ++s) {
           const int off = dma_a + s * a_step + k0 * ESZ;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, MSIGN_LDS(&lds[buf][s * NT + uw * 64]), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rP, MSIGN_LDS(stage + s * NT + uw * 64), 16, off, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int s = 0; s < BCH; ++s) {
         const int off = dma_b + s * b_step + k0 * ESZ;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, MSIGN_LDS(&lds[buf][BM * CPR + s * NT + uw * 64]), 16, off,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, MSIGN_LDS(stage + BM * CPR + s * NT + uw * 64), 16, off,
                                                  0, 0, 0);
       }
     };
-    if (nk > 0) issue(0, kt0 * KTE);
+    // (one step: the loads into `wr` and the reads from `rd` are declared
+    // not to alias, so the reads need not wait for the loads in flight)
+    auto step = [&](const u32x4* __restrict__ rd, u32x4* __restrict__ wr, bool load_next, int k_next) {
+      if (load_next) issue(wr, k_next);
+      compute(rd);
+    };
+    if (nk > 0) issue(lds[0], kt0 * KTE);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     for (int j = 0; j < nk; ++j) {
-      if (j + 1 < nk) issue((j + 1) & 1, (kt0 + j + 1) * KTE);
-      compute(j & 1);
+      step(lds[j & 1], lds[(j + 1) & 1], j + 1 < nk, (kt0 + j + 1) * KTE);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   } else {
@@ -828,7 +833,7 @@ gemm_nt_kernel(const GemmParams p) {
   auto iter = [&](int j, auto S) {
     constexpr int s = decltype(S)::value;  // j % NST
     gload(stg[s], (kt0 + (j + NST) * KW) * KTE);
-    if (KW == 1 || j * KW + kw < nk) compute(j & 1);
+    if (KW == 1 || j * KW + kw < nk) compute(lds[j & 1]);
     if (j + 1 < ns) lstore(stg[(s + 1) % NST], (j + 1) & 1);
     __syncthreads();
   };

@@ -210,11 +210,8 @@ enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3 };
 // with 16 waves of 64 x 64 (4 waves per SIMD hide LDS and MFMA latency; the
 // 64 accumulators per lane stay in VGPRs; one block per CU) when the problem
 // has at least one full round of such tiles for the 256 CUs, with 128-byte
-// K slices (half the barriers of 64-byte slices): triangle products load
-// them straight into a 2-stage LDS ring (buffer_load ... lds), rectangular
-// ones through one slice of register prefetch (the compiler would make the
-// transpose reads of the K-major operand wait for the direct loads);
-// otherwise 128 x 128 tiles
+// K slices (half the barriers of 64-byte slices) loaded straight into a
+// 2-stage LDS ring (buffer_load ... lds); otherwise 128 x 128 tiles
 // with 4 waves of 64 x 64 (two blocks per CU) if those fill the CUs, else
 // 64 x 64 tiles shared along K by four waves (latency-bound problems).
 // These two use 64-byte K slices with two slices of register prefetch.
@@ -315,7 +312,7 @@ hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st)
 // as X^T).
 template <typename T>
 hipError_t launch_nt_at(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
-  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 1, false, 1, true>(q, l, st);
+  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 0, false, 1, true>(q, l, st);
   if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, false, 1, true>(q, l, st);
   return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, true>(q, l, st);
 }
