@@ -212,9 +212,10 @@ enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3 };
 // has at least one full round of such tiles for the 256 CUs, with 128-byte
 // K slices (half the barriers of 64-byte slices) loaded straight into a
 // 2-stage LDS ring (buffer_load ... lds); otherwise 128 x 128 tiles
-// with 4 waves of 64 x 64 (two blocks per CU) if those fill the CUs, else
-// 64 x 64 tiles shared along K by four waves (latency-bound problems).
-// These two use 64-byte K slices with two slices of register prefetch.
+// with 4 waves of 64 x 64 (two blocks per CU; 64-byte K slices, loaded the
+// same way) if those fill the CUs, else 64 x 64 tiles shared along K by
+// four waves (latency-bound problems; 64-byte K slices with two slices of
+// register prefetch).
 constexpr int kCUs = 256;
 constexpr int kSplitMax = 8;
 
@@ -304,7 +305,7 @@ template <typename T, bool TRI>
 hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
   static_assert(TRI, "rectangular products go through launch_nt_at");
   if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 0, TRI, 1, false>(q, l, st);
-  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, TRI, 1, false>(q, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 0, TRI, 1, false>(q, l, st);
   return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI, 4, false>(q, l, st);
 }
 
@@ -313,7 +314,7 @@ hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st)
 template <typename T>
 hipError_t launch_nt_at(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
   if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 0, false, 1, true>(q, l, st);
-  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 2, false, 1, true>(q, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 0, false, 1, true>(q, l, st);
   return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, true>(q, l, st);
 }
 
