@@ -94,3 +94,18 @@ def test_moe_experts(method, cdt):
         _check_samples(x, y, 2e-2, f"moe {method} group {gi}")
         del x, y
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_big_tiles_with_ragged_edges():
+    """6000 x 6500: 256 x 256 tiles whose last row and column of tiles stick
+    out of the matrix (the epilogue's bounds-checked path next to the staged
+    one), checked against the oracle; tall input as well."""
+    M = require_gpu()
+    x = S.small_case(6000, 6500, "bf16", 4242, batch=1, noise_std=1.0, spike_rank=0)
+    for label, xi in (("wide", x), ("tall", x.transpose(-1, -2).contiguous())):
+        announce(f"msign_ns 6000x6500 {label}")
+        y = M.msign_ns(xi.cuda(), compute_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        err = O.max_rel_fro_error(f64(y), O.ns(f64(xi)))
+        assert err <= 2e-2, (label, err)
