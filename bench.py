@@ -34,7 +34,9 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense MFM
 HBM_GBS = 8000.0
 
 # name -> (workload, method, compute dtype, restarts); "ns_init" is standard NS
-# with the improved initial normalisation
+# with the improved initial normalisation, "muon_ns" a whole Muon step
+# (momentum, msign by NS, parameter update) with the workload as gradients.
+# Workloads of several shape groups run as one grouped call per step.
 CASES = {
     "c3_ns_bf16": ("c3_8192x8192_bf16", "ns", "bf16", ()),
     "c3_ns_init_bf16": ("c3_8192x8192_bf16", "ns_init", "bf16", ()),
@@ -43,6 +45,7 @@ CASES = {
     "c2_ns_bf16": ("c2_1024x4096_bf16", "ns", "bf16", ()),
     "c2_gram_f16": ("c2_1024x4096_bf16", "gram", "f16", (2,)),
     "c4_ns_bf16": ("c4_block_bf16", "ns", "bf16", ()),
+    "c4_muon_ns_bf16": ("c4_block_bf16", "muon_ns", "bf16", ()),
     "c5_ns_bf16": ("c5_moe_f16", "ns", "bf16", ()),
     "c5_gram_f16": ("c5_moe_f16", "gram", "f16", (2,)),
 }
@@ -67,7 +70,8 @@ def class_flops(n, m):
 # traffic figure is reported only while the kernel sources hash to the value
 # recorded with it; after any change to them it is stale and `traffic` is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_rect_8192x8192_bf16_traffic.md")
-KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "msign_api.hip")
+KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "init_scale.hpp", "launch.hpp", "launch_impl.hpp", "muon.hpp",
+                  "msign_api.hip", "products_grouped.hip", "products_single.hip")
 
 
 def kernel_source_hash():
@@ -164,6 +168,9 @@ def cpu_baseline(wl, method, sample_seconds=30.0):
             t0 = time.perf_counter()
             if method == "ns":
                 O.ns_single(m, steps=steps_run)
+            elif method == "muon_ns":
+                O.muon_step(0.02 * m, m, np.zeros_like(m), 0.95, 0.02,
+                            msign=lambda v: O.ns_single(v, steps=steps_run))
             elif method == "ns_init":
                 O.ns_improved_init_single(m, steps=steps_run)
             else:
@@ -192,19 +199,32 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
     wl, xs = load_inputs(workload, dev)
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cdt]
     outs = [torch.empty_like(x) for x in xs]
+    grouped = len(xs) > 1
+    if method == "muon_ns":
+        gen = torch.Generator(device=dev).manual_seed(77)
+        params = [(0.02 * torch.randn(x.shape, generator=gen, device=dev)).to(x.dtype) for x in xs]
+        moms = [torch.zeros(x.shape, dtype=torch.float32, device=dev) for x in xs]
     wss = []
-    for x in xs:
-        b, r, c = x.shape
+    if not grouped and method != "muon_ns":
+        b, r, c = xs[0].shape
         nb = (M.ns_workspace_bytes(b, r, c, tdt) if method.startswith("ns")
               else M.gram_ns_workspace_bytes(b, r, c, tdt))
         wss.append(torch.empty(max(nb, 1), dtype=torch.uint8, device=dev))
 
     def one_step():
-        for x, y, ws in zip(xs, outs, wss):
-            if method.startswith("ns"):
-                M.msign_ns(x, compute_dtype=tdt, out=y, workspace=ws, improved_init=(method == "ns_init"))
-            else:
-                M.msign_gram_ns(x, compute_dtype=tdt, restart_after=restarts, out=y, workspace=ws)
+        # grouped calls size their workspace themselves (torch's caching
+        # allocator hands back the same block every step)
+        if method == "muon_ns":
+            M.muon_step(params, xs, moms, lr=0.02, mu=0.95, method="ns", compute_dtype=tdt)
+        elif grouped and method.startswith("ns"):
+            M.msign_ns_grouped(xs, compute_dtype=tdt, outs=outs, improved_init=(method == "ns_init"))
+        elif grouped:
+            M.msign_gram_ns_grouped(xs, compute_dtype=tdt, restart_after=restarts, outs=outs)
+        elif method.startswith("ns"):
+            M.msign_ns(xs[0], compute_dtype=tdt, out=outs[0], workspace=wss[0],
+                       improved_init=(method == "ns_init"))
+        else:
+            M.msign_gram_ns(xs[0], compute_dtype=tdt, restart_after=restarts, out=outs[0], workspace=wss[0])
 
     for _ in range(warmup):
         one_step()
@@ -259,7 +279,10 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cdt, "data": "synthetic",
-        "config": {"workload": workload, "case": name, "method": {"ns": "msign_ns", "ns_init": "msign_ns_ex(IMPROVED_INIT)", "gram": "msign_gram_ns"}[method],
+        "config": {"workload": workload, "case": name,
+                   "method": {"ns": "msign_ns", "ns_init": "msign_ns_ex(IMPROVED_INIT)", "gram": "msign_gram_ns",
+                              "muon_ns": "muon_step(MUON_NS)"}[method]
+                   + ("_grouped" if grouped and method != "muon_ns" else ""),
                    "shapes": shapes, "T": 5, "compute": cdt, "restart_after": list(restarts),
                    "parallelism": "single GPU"},
         "effective_tflops": eff_tflops,
@@ -275,10 +298,9 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
         rec["kernels_one_step"] = per
         tot, cnt = ktime[dom]
         if cnt:
-            # every group's call makes the same number of launches of a class;
-            # one launch processes that group's whole batch
-            groups = len(xs)
-            flops_per_launch = cls_flops[dom] / groups
+            # one launch of a class processes every group's whole batch (a
+            # grouped launch when there are several groups)
+            flops_per_launch = cls_flops[dom]
             avg_s = tot / cnt / 1e3
             ach = flops_per_launch / avg_s / 1e12
             rec["roofline"] = {"bound": "mfma", "kernel": f"gemm_nt_kernel ({dom})", "achieved": ach,

@@ -13,7 +13,10 @@
  *        out of Z, §3.4 Algorithm 2, §4 symmetric GEMM C <- aAB + bC + gI.
  *   [NB] nil9.net, flash-muon excerpt: the X X^T operator that computes only
  *        upper-triangle tiles and stores each tile's transpose into the
- *        mirrored lower-triangle tile.
+ *        mirrored lower-triangle tile; NS applied to the gradient or its
+ *        momentum.
+ *   [MS] the Mousse page (anti-entrophic.github.io/posts/10054.html),
+ *        §标准 Muon 算法: the Muon update is -msign of the matrix.
  *
  * Conventions shared by every entry point:
  *   - Layout: contiguous row-major [batch, rows, cols]; matrix b starts at
@@ -160,6 +163,100 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch,
                              hipStream_t stream);
 
 /*
+ * Grouped calls: one msign over several batches of different shapes at once
+ * (the parameter list of an optimizer step holds a few shape groups, e.g.
+ * the square and the 3.5x-wide matrices of a transformer block).  Every
+ * matrix product of the iteration is ONE kernel launch over the tiles of
+ * all groups (longest contraction first), so a small group fills the CUs
+ * that a large group's last round of tiles leaves idle, and the launch
+ * count does not grow with the number of groups.  Each matrix gets the
+ * result that a call on its group alone would give, up to the last bits
+ * (the K split of the last round of tiles depends on the whole launch).
+ *
+ * Group g: x, y device [batch, rows, cols] in io_dtype, as in msign_ns (y ==
+ * x allowed).  Groups with batch, rows or cols equal to 0 are skipped.  An
+ * output may not overlap any other group's input or output (MSIGN_ERR_ALIAS);
+ * inputs may overlap each other.  io_dtype, compute_dtype, steps, coeffs,
+ * eps (and flags or the restart list) are shared by all groups.
+ *   groups    HOST array of ngroups descriptors, read before the call returns.
+ *   ngroups   1..MSIGN_MAX_GROUPS; with 1 these are msign_ns_ex and
+ *             msign_gram_ns, workspace size included.
+ * An invalid group is reported with its index in msign_last_error().
+ */
+#define MSIGN_MAX_GROUPS 4
+
+typedef struct {
+  const void* x;
+  void* y;
+  int64_t batch, rows, cols;
+} msign_group_t;
+
+/* Workspace of a grouped call; 0 if every group is empty, (size_t)-1 for an
+ * invalid count, size or dtype. */
+size_t msign_ns_grouped_workspace_bytes(const msign_group_t* groups, int32_t ngroups,
+                                        int32_t compute_dtype);
+size_t msign_gram_ns_grouped_workspace_bytes(const msign_group_t* groups, int32_t ngroups,
+                                             int32_t compute_dtype);
+
+msign_status_t msign_ns_grouped(const msign_group_t* groups, int32_t ngroups,
+                                int32_t io_dtype, int32_t compute_dtype,
+                                int32_t steps, const float* coeffs, float eps,
+                                uint32_t flags, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+msign_status_t msign_gram_ns_grouped(const msign_group_t* groups, int32_t ngroups,
+                                     int32_t io_dtype, int32_t compute_dtype,
+                                     int32_t steps, const float* coeffs, float eps,
+                                     const int32_t* restart_after, int32_t n_restarts,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
+ * muon_step - one Muon optimizer step over up to MSIGN_MAX_GROUPS parameter
+ * groups ([GR] §1.1 names the momentum coefficient mu, the learning rate
+ * eta and M_0 = 0, its formula is lost in the text; [MS] §标准 Muon 算法:
+ * the update is -msign; [NB]: NS acts on the gradient or its momentum).
+ * Read as, for every matrix of every group:
+ *     M <- mu M + G;   W <- W - lr msign(M)
+ * with msign by standard NS (MUON_NS, as msign_ns_grouped with `flags`) or
+ * Gram NS (MUON_GRAM, as msign_gram_ns_grouped; flags must be 0), all groups'
+ * products in grouped launches.  M is fp32; msign(M) is formed in fp32 in the
+ * workspace and W is rounded once, to io_dtype.
+ *
+ * Group g: w (parameters, updated in place) and g (gradient), device
+ * [batch, rows, cols] in io_dtype; m (momentum, updated in place), device
+ * [batch, rows, cols] fp32, 16-byte alignment recommended.  Empty groups
+ * are skipped.  w and m may overlap no other buffer of the step and no
+ * buffer may overlap the workspace (MSIGN_ERR_ALIAS).
+ *   mu, lr      finite.
+ *   method      MUON_NS or MUON_GRAM.
+ *   other arguments as in msign_ns_grouped / msign_gram_ns_grouped.
+ * A non-OK status from argument checks means nothing was launched.
+ */
+#define MUON_NS 0
+#define MUON_GRAM 1
+
+typedef struct {
+  void* w;
+  const void* g;
+  float* m;
+  int64_t batch, rows, cols;
+} muon_group_t;
+
+/* Workspace of muon_step; 0 if every group is empty, (size_t)-1 for an
+ * invalid count, size, method or dtype. */
+size_t muon_step_workspace_bytes(const muon_group_t* groups, int32_t ngroups,
+                                 int32_t method, int32_t compute_dtype);
+
+msign_status_t muon_step(const muon_group_t* groups, int32_t ngroups,
+                         int32_t io_dtype, float mu, float lr, int32_t method,
+                         int32_t compute_dtype, int32_t steps,
+                         const float* coeffs, float eps, uint32_t flags,
+                         const int32_t* restart_after, int32_t n_restarts,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * syrk_xxt - C = alpha X X^T + beta D + gamma I for each matrix of a batch
  * ([NB] X X^T operator; [GR] §4 fused form C <- aAB + bC + gI with A = X,
  * B = X^T).
@@ -201,7 +298,8 @@ const char* msign_version(void);
  * above is bracketed by a pair of events recorded on the call's stream;
  * msign_kernel_timing_read() waits for them, adds their durations to
  * per-class totals and clears the queue.
- * Classes: 0 = normalise (sum of squares + scale/cast), 1 = X X^T (triangle),
+ * Classes: 0 = normalise (sum of squares + scale/cast) and the elementwise
+ * passes of muon_step, 1 = X X^T (triangle),
  * 2 = n x n triangle products (A^2 / Gram R, Q, Z, RZ updates), 3 = the
  * rectangular product (B X, Q X).
  *   msign_kernel_timing_enable   mask of classes to time (bit k = class k,

@@ -5,10 +5,11 @@ marshals arguments; all computation runs in the HIP library, which must be
 built (`python -m msign_newton_schulz_amd.build`) before use.
 """
 
-from ._binding import (F32, BF16, F16, LIB_PATH, MsignError, gram_ns_workspace_bytes,  # noqa: F401
-                       kernel_timing, library, msign_gram_ns, msign_ns, ns_workspace_bytes,
+from ._binding import (F32, BF16, F16, LIB_PATH, MAX_GROUPS, MsignError,  # noqa: F401
+                       gram_ns_workspace_bytes, kernel_timing, library, msign_gram_ns,
+                       msign_gram_ns_grouped, msign_ns, msign_ns_grouped, muon_step, ns_workspace_bytes,
                        read_kernel_timing, syrk_xxt, version)
 
-__all__ = ["msign_ns", "msign_gram_ns", "syrk_xxt", "MsignError", "library", "version",
+__all__ = ["msign_ns", "msign_gram_ns", "msign_ns_grouped", "msign_gram_ns_grouped", "muon_step", "syrk_xxt", "MsignError", "library", "version",
            "ns_workspace_bytes", "gram_ns_workspace_bytes", "kernel_timing", "read_kernel_timing",
-           "LIB_PATH", "F32", "BF16", "F16"]
+           "LIB_PATH", "MAX_GROUPS", "F32", "BF16", "F16"]

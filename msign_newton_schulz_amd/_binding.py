@@ -32,6 +32,23 @@ class MsignError(RuntimeError):
         super().__init__(f"libmsign: {_STATUS.get(status, status)}: {detail}")
 
 
+MAX_GROUPS = 4  # MSIGN_MAX_GROUPS
+
+
+class _Group(ctypes.Structure):
+    """msign_group_t"""
+    _fields_ = [("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("batch", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class _MuonGroup(ctypes.Structure):
+    """muon_group_t"""
+    _fields_ = [("w", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("batch", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+MUON_NS, MUON_GRAM = 0, 1
+
 _lib = None
 
 
@@ -59,6 +76,20 @@ def _load():
     lib.msign_gram_ns.restype = ctypes.c_int
     lib.syrk_xxt.argtypes = [vp, vp, i64, i64, i64, i32, f, vp, f, f, vp, sz, vp]
     lib.syrk_xxt.restype = ctypes.c_int
+    gp = ctypes.POINTER(_Group)
+    lib.msign_ns_grouped_workspace_bytes.argtypes = [gp, i32, i32]
+    lib.msign_ns_grouped_workspace_bytes.restype = sz
+    lib.msign_gram_ns_grouped_workspace_bytes.argtypes = [gp, i32, i32]
+    lib.msign_gram_ns_grouped_workspace_bytes.restype = sz
+    lib.msign_ns_grouped.argtypes = [gp, i32, i32, i32, i32, fp, f, ctypes.c_uint32, vp, sz, vp]
+    lib.msign_ns_grouped.restype = ctypes.c_int
+    lib.msign_gram_ns_grouped.argtypes = [gp, i32, i32, i32, i32, fp, f, ip, i32, vp, sz, vp]
+    lib.msign_gram_ns_grouped.restype = ctypes.c_int
+    mp = ctypes.POINTER(_MuonGroup)
+    lib.muon_step_workspace_bytes.argtypes = [mp, i32, i32, i32]
+    lib.muon_step_workspace_bytes.restype = sz
+    lib.muon_step.argtypes = [mp, i32, i32, f, f, i32, i32, i32, fp, f, ctypes.c_uint32, ip, i32, vp, sz, vp]
+    lib.muon_step.restype = ctypes.c_int
     lib.msign_status_string.argtypes = [ctypes.c_int]
     lib.msign_status_string.restype = ctypes.c_char_p
     lib.msign_last_error.argtypes = []
@@ -201,6 +232,117 @@ def msign_gram_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-
                                _stream_handle(x.device))
     _check(st)
     return y
+
+
+def _groups(xs, outs):
+    """Contiguous inputs, outputs and the msign_group_t array of a grouped call."""
+    xs = [x.contiguous() for x in xs]
+    if not 1 <= len(xs) <= MAX_GROUPS:
+        raise ValueError(f"a grouped call takes 1..{MAX_GROUPS} tensors, got {len(xs)}")
+    _check_cuda(*xs)
+    if len({x.dtype for x in xs}) != 1 or len({x.device for x in xs}) != 1:
+        raise ValueError("grouped tensors must share dtype and device")
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    outs = list(outs)
+    if len(outs) != len(xs):
+        raise ValueError("outs needs one tensor per input")
+    arr = (_Group * len(xs))()
+    for i, (x, y) in enumerate(zip(xs, outs)):
+        _check_cuda(y)
+        if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+            raise ValueError("each out must be contiguous with the shape and dtype of its input")
+        batch, rows, cols = _batch_dims(x)
+        arr[i] = _Group(x.data_ptr(), y.data_ptr(), batch, rows, cols)
+    return xs, outs, arr
+
+
+def msign_ns_grouped(xs: Sequence[torch.Tensor], steps: int = 5, coeffs=None, eps: float = 1e-20,
+                     compute_dtype=torch.bfloat16, outs: Optional[Sequence[torch.Tensor]] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     improved_init: bool = False) -> list:
+    """msign_ns over up to MAX_GROUPS tensors of different shapes in one call
+    (C ABI `msign_ns_grouped`): each product of the iteration is one launch
+    over all of them.  Returns one output per input."""
+    lib = _load()
+    xs, outs, arr = _groups(xs, outs)
+    io, cdt = _dt(xs[0].dtype), _dt(compute_dtype)
+    nbytes = lib.msign_ns_grouped_workspace_bytes(arr, len(xs), cdt)
+    ws = _workspace(nbytes, xs[0].device, workspace)
+    _check_cuda(ws)
+    carr = _coeff_array(coeffs, steps)
+    with torch.cuda.device(xs[0].device):
+        st = lib.msign_ns_grouped(arr, len(xs), io, cdt, steps, carr, float(eps),
+                                  IMPROVED_INIT if improved_init else 0, ws.data_ptr(), ws.numel(),
+                                  _stream_handle(xs[0].device))
+    _check(st)
+    return outs
+
+
+def msign_gram_ns_grouped(xs: Sequence[torch.Tensor], steps: int = 5, coeffs=None, eps: float = 1e-20,
+                          compute_dtype=torch.float16, restart_after: Sequence[int] = (2,),
+                          outs: Optional[Sequence[torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None) -> list:
+    """msign_gram_ns over up to MAX_GROUPS tensors of different shapes in one
+    call (C ABI `msign_gram_ns_grouped`).  Returns one output per input."""
+    lib = _load()
+    xs, outs, arr = _groups(xs, outs)
+    io, cdt = _dt(xs[0].dtype), _dt(compute_dtype)
+    nbytes = lib.msign_gram_ns_grouped_workspace_bytes(arr, len(xs), cdt)
+    ws = _workspace(nbytes, xs[0].device, workspace)
+    _check_cuda(ws)
+    carr = _coeff_array(coeffs, steps)
+    rs = [int(r) for r in restart_after]
+    rarr = (ctypes.c_int32 * len(rs))(*rs) if rs else None
+    with torch.cuda.device(xs[0].device):
+        st = lib.msign_gram_ns_grouped(arr, len(xs), io, cdt, steps, carr, float(eps), rarr, len(rs),
+                                       ws.data_ptr(), ws.numel(), _stream_handle(xs[0].device))
+    _check(st)
+    return outs
+
+
+def muon_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
+              moms: Sequence[torch.Tensor], *, lr: float, mu: float, method: str = "ns",
+              steps: int = 5, coeffs=None, eps: float = 1e-20, compute_dtype=None,
+              restart_after: Sequence[int] = (2,), improved_init: bool = False,
+              workspace: Optional[torch.Tensor] = None) -> None:
+    """One Muon step in place over up to MAX_GROUPS parameter tensors (C ABI
+    `muon_step`): for every matrix over the last two dims, m <- mu m + g and
+    w <- w - lr msign(m), msign by standard NS (`method="ns"`, bf16 products
+    by default) or Gram NS (`"gram"`, fp16 products, restart after step 2 by
+    default).  Parameters and gradients share one dtype; momenta are fp32."""
+    lib = _load()
+    params, grads, moms = list(params), list(grads), list(moms)
+    if not (len(params) == len(grads) == len(moms)) or not 1 <= len(params) <= MAX_GROUPS:
+        raise ValueError(f"muon_step takes 1..{MAX_GROUPS} (param, grad, momentum) triples")
+    if method not in ("ns", "gram"):
+        raise ValueError("method must be 'ns' or 'gram'")
+    _check_cuda(*params, *grads, *moms, workspace)
+    io = _dt(params[0].dtype)
+    arr = (_MuonGroup * len(params))()
+    for i, (w, g, m) in enumerate(zip(params, grads, moms)):
+        if g.shape != w.shape or m.shape != w.shape:
+            raise ValueError("each gradient and momentum must have its parameter's shape")
+        if w.dtype != params[0].dtype or g.dtype != w.dtype or m.dtype != torch.float32:
+            raise ValueError("parameters and gradients share one dtype; momenta are float32")
+        if not (w.is_contiguous() and g.is_contiguous() and m.is_contiguous()):
+            raise ValueError("parameters, gradients and momenta must be contiguous")
+        batch, rows, cols = _batch_dims(w)
+        arr[i] = _MuonGroup(w.data_ptr(), g.data_ptr(), m.data_ptr(), batch, rows, cols)
+    meth = MUON_NS if method == "ns" else MUON_GRAM
+    if compute_dtype is None:
+        compute_dtype = torch.bfloat16 if method == "ns" else torch.float16
+    cdt = _dt(compute_dtype)
+    nbytes = lib.muon_step_workspace_bytes(arr, len(params), meth, cdt)
+    ws = _workspace(nbytes, params[0].device, workspace)
+    carr = _coeff_array(coeffs, steps)
+    rs = [int(r) for r in restart_after] if method == "gram" else []
+    rarr = (ctypes.c_int32 * len(rs))(*rs) if rs else None
+    flags = IMPROVED_INIT if improved_init else 0
+    with torch.cuda.device(params[0].device):
+        st = lib.muon_step(arr, len(params), io, float(mu), float(lr), meth, cdt, steps, carr, float(eps),
+                           flags, rarr, len(rs), ws.data_ptr(), ws.numel(), _stream_handle(params[0].device))
+    _check(st)
 
 
 def syrk_xxt(x: torch.Tensor, alpha: float = 1.0, d: Optional[torch.Tensor] = None,

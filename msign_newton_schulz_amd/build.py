@@ -1,8 +1,10 @@
 """Builds libmsign.so in-tree with hipcc for gfx950.
 
-The library is one translation unit (csrc/msign_api.hip includes the kernel
-headers).  The output goes to a temporary file that is renamed into place, so
-a failed build never leaves a half-written library behind.
+Each csrc/*.hip file is one translation unit (the host API, and the product
+kernels for single and for grouped launches), compiled in parallel to
+objects in a temporary folder and linked into one shared library.  The output
+goes to a temporary file that is renamed into place, so a failed build never
+leaves a half-written library behind.
 """
 
 from __future__ import annotations
@@ -11,16 +13,17 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "msign_api.hip")
+CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmsign.so")
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are kept out of the generated code on purpose.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]
 
@@ -38,21 +41,47 @@ def sources():
             if f.endswith((".hip", ".hpp", ".h"))] + [os.path.join(INCLUDE, "msign.h")]
 
 
+def translation_units():
+    return [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
+
+
+def _run(cmds, verbose):
+    """Run the commands in parallel; raise with the first failure's output."""
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    failed = None
+    for cmd, p in zip(cmds, procs):
+        out, _ = p.communicate()
+        noise = [ln for ln in out.splitlines() if ln.strip() and "packed-fp32-ops" not in ln]
+        if p.returncode != 0 and failed is None:
+            failed = (p.returncode, out)
+        elif verbose and noise:
+            sys.stderr.write("\n".join(noise) + "\n")
+    if failed:
+        sys.stderr.write(failed[1])
+        raise RuntimeError(f"hipcc failed with exit code {failed[0]}")
+
+
 def build(verbose: bool = False, extra_flags=None) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + list(extra_flags or []) + ["-I", INCLUDE, SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    noise = [ln for ln in (res.stdout + res.stderr).splitlines()
-             if ln.strip() and "packed-fp32-ops" not in ln]
-    if verbose and noise:
-        sys.stderr.write("\n".join(noise) + "\n")
+    cc = hipcc()
+    flags = FLAGS + list(extra_flags or []) + ["-I", INCLUDE]
+    with tempfile.TemporaryDirectory(prefix="msign_build_") as objdir:
+        objs, cmds = [], []
+        for src in translation_units():
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmds.append([cc] + flags + ["-c", src, "-o", obj])
+        try:
+            _run(cmds, verbose)
+            _run([[cc, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp]], verbose)
+        except Exception:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise
     os.replace(tmp, LIB)
     return LIB
 

@@ -78,6 +78,20 @@ struct GemmParams {
   float* sumsq;
 };
 
+// One launch may cover up to kMaxGroups problems of one product kind
+// and tile configuration (a grouped launch): group g owns the blocks from
+// bstart[g] up to the next group's first block, and numbers its tiles, its
+// K split and its partial sums on its own.  Unused entries have bstart =
+// INT32_MAX.  A single product is launched with a one-entry table (NG = 1:
+// the kernel argument stays small and there is no lookup).
+constexpr int kMaxGroups = 4;
+
+template <int NG>
+struct GemmGroups {
+  GemmParams g[NG];
+  int32_t bstart[NG];
+};
+
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
   static __device__ __forceinline__ void run(f32x4& acc, const u32x4& a, const u32x4& b) {
@@ -544,9 +558,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
   }
 }
 
+// Block b of the launch of problem p (b counts from the problem's first
+// block).
 template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW, bool AT>
-__global__ void __launch_bounds__(WGM * WGN * KW * 64)
-gemm_nt_kernel(const GemmParams p) {
+__device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) {
   constexpr int NT = WGM * WGN * KW * 64;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int FM = WM / 16, FN = WN / 16;
@@ -584,7 +599,6 @@ gemm_nt_kernel(const GemmParams p) {
   // ---- tile (or K part of a tile) of this block ----
   // Whole tiles come first in block order, renumbered XCD-contiguously among
   // themselves; the K parts of the split tiles follow, dealt round-robin.
-  const int b = blockIdx.x;
   int L, part = -1, unit = 0;
   if (b < p.nfull) {
     L = xcd_contiguous(b, p.nfull);
@@ -903,6 +917,23 @@ gemm_nt_kernel(const GemmParams p) {
   epilogue<BM, BN, WGM, WGN, TRI>(p, L, bz, ti, tj, acc, wave, reinterpret_cast<float*>(&lds[0][0]));
 }
 
+template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW, bool AT, int NG>
+__global__ void __launch_bounds__(WGM * WGN * KW * 64)
+gemm_nt_kernel(const GemmGroups<NG> groups) {
+  if constexpr (NG == 1) {
+    gemm_nt_block<T, BM, BN, WGM, WGN, BKB, NST, TRI, KW, AT>(groups.g[0], (int)blockIdx.x);
+  } else {
+    // The table is read in place from the kernel-argument segment (it is
+    // the first argument): indexing the by-value argument with the block's
+    // group would make the compiler copy the whole table to scratch memory.
+    const GemmGroups<NG>& G = *(const GemmGroups<NG>*)__builtin_amdgcn_kernarg_segment_ptr();
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < NG; ++i) gi += (int)blockIdx.x >= G.bstart[i] ? 1 : 0;
+    gemm_nt_block<T, BM, BN, WGM, WGN, BKB, NST, TRI, KW, AT>(G.g[gi], (int)blockIdx.x - G.bstart[gi]);
+  }
+}
+
 // Second pass for split tiles.  Block (t, w) takes wave w's fragments of
 // split tile t; its wave q handles fragment row fm = q: it adds the tile's
 // parts in part order (fixed, so the result is bit-stable) and runs the
@@ -943,60 +974,6 @@ gemm_nt_reduce_kernel(const GemmParams p) {
   epilogue_rows<BM, BN, WGM, WGN, TRI, 1>(p, bz, ti, tj, w, fm, acc, sq);
   if (TRI && p.sumsq != nullptr)
     wave_sum_store((ti != tj ? 2.f : 1.f) * sq[0], sumsq_slot<BM, WGM, WGN>(p, p.nfull + t, w, fm));
-}
-
-// Improved initial normalisation ("msign算子的Newton-Schulz迭代（上）"
-// §改良初值): after the first A = X X^T and A2 = A A, the iterate is divided
-// by s = (||A2||_F^2 + eps)^(1/8), the fourth root of ||(X X^T)^2||_F.
-//
-// init_scale_kernel: one block per matrix adds that matrix's acc^2 slots of
-// the A A launch `q` (the slot layout of GemmParams::sumsq, `slots` per
-// tile, padding blocks of the folded triangle skipped) in a fixed order and
-// writes scales[4 bz + k] = s^-(1, 2, 4)[k].
-__global__ void __launch_bounds__(256)
-init_scale_kernel(const GemmParams q, int32_t slots, float eps, float* scales) {
-  const int64_t b = blockIdx.x;
-  const int tid = threadIdx.x;
-  float acc = 0.f;
-  for (int64_t i = tid; i < (int64_t)q.tpm * slots; i += 256) {
-    const int L = (int)(b * q.tpm + i / slots);
-    int64_t bz;
-    int ti, tj;
-    if (tile_of<true>(q, L, bz, ti, tj)) acc += q.sumsq[(int64_t)L * slots + i % slots];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  __shared__ float ws[4];
-  if ((tid & 63) == 0) ws[tid >> 6] = acc;
-  __syncthreads();
-  if (tid == 0) {
-    const float sum = ((ws[0] + ws[1]) + ws[2]) + ws[3];
-    const float s = sqrtf(sqrtf(sqrtf(sum + eps)));
-    const float r = 1.f / s;
-    scales[4 * b] = r;
-    scales[4 * b + 1] = r * r;
-    scales[4 * b + 2] = (r * r) * (r * r);
-    scales[4 * b + 3] = 0.f;
-  }
-}
-
-// B <- (b s^-2) A + (c s^-4) B over `per` elements (a multiple of 4) of each
-// matrix: the first B = b A + c A2 of the normalised iterate, with A2 held
-// in B.  Four consecutive elements per thread.
-__global__ void __launch_bounds__(256)
-init_combine_kernel(const void* A, void* B, int64_t per, int32_t dt, float b, float c,
-                    const float* scales) {
-  const int64_t bz = blockIdx.y;
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= per) return;
-  const float fa = b * scales[4 * bz + 1], fb = c * scales[4 * bz + 2];
-  const int64_t base = bz * per + e;
-  float va[4], vb[4], w[4];
-  load_vec4(A, base, dt, va);
-  load_vec4(B, base, dt, vb);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = fa * va[k] + fb * vb[k];
-  store_vec4(B, base, dt, w);
 }
 
 }  // namespace msign

@@ -24,6 +24,9 @@
 #include "../../include/msign.h"
 #include "common.hpp"
 #include "gemm_nt.hpp"
+#include "init_scale.hpp"
+#include "launch.hpp"
+#include "muon.hpp"
 #include "normalize.hpp"
 
 #include <atomic>
@@ -71,10 +74,11 @@ Shape canon(int64_t rows, int64_t cols) {
   return s;
 }
 
+struct Prob;
 // K-split scratch of the products of one NS or Gram call, and the acc^2
 // slots of the first A A product (defined below).
-size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt);
-size_t init_sumsq_floats(const Shape& s, int64_t batch, int32_t cdt);
+size_t split_scratch(const Prob* pr, int ng, int32_t cdt);
+size_t init_sumsq_floats(const Shape& s, int64_t batch);
 
 int32_t norm_blocks(int64_t count) {
   int64_t nb = (count + 16383) / 16384;
@@ -92,60 +96,73 @@ struct Carver {
   }
 };
 
-struct NsPlan {
+// One problem of a (grouped) call: batch matrices of rows x cols.
+struct Prob {
+  const void* x;
+  void* y;
+  int64_t batch, rows, cols;
   Shape s;
-  int32_t nblk;
-  size_t x32[2], xh[2], a, b, partial, sumsq, scales, split, split_bytes, total;
 };
 
-NsPlan plan_ns(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
-  NsPlan p;
-  p.s = canon(rows, cols);
-  p.nblk = norm_blocks(rows * cols);
+// Workspace regions of one problem of an NS call (offsets from the call's
+// workspace base).  `split` is the K-split scratch of the call's launches:
+// the problem's own when it is alone, else one region shared by all.
+struct NsPlan {
+  int32_t nblk;
+  size_t x32[2], xh[2], a, b, partial, sumsq, scales;
+};
+
+struct GramPlan {
+  int32_t nblk;
+  size_t xh[2], r, z, rz, q[2], partial;
+};
+
+template <typename P>
+struct CallPlan {
+  int ng;
+  P p[MSIGN_MAX_GROUPS];
+  size_t split, split_bytes, total;
+};
+
+void plan_ns_regions(const Prob& pr, int32_t cdt, Carver& c, NsPlan& p) {
+  p.nblk = norm_blocks(pr.rows * pr.cols);
   const size_t cs = dt_size(cdt);
-  const size_t nm = (size_t)batch * p.s.np * p.s.mp, nn = (size_t)batch * p.s.np * p.s.np;
-  Carver c;
+  const size_t nm = (size_t)pr.batch * pr.s.np * pr.s.mp, nn = (size_t)pr.batch * pr.s.np * pr.s.np;
   for (int i = 0; i < 2; ++i) {
     p.x32[i] = c.take(nm * 4);
     p.xh[i] = c.take(nm * cs);
   }
   p.a = c.take(nn * cs);
   p.b = c.take(nn * cs);
-  p.partial = c.take((size_t)batch * p.nblk * 4);
-  p.sumsq = c.take(init_sumsq_floats(p.s, batch, cdt) * 4);
-  p.scales = c.take((size_t)batch * 4 * 4);
-  p.split_bytes = split_scratch(p.s, batch, cdt);
-  p.split = c.take(p.split_bytes);
-  p.total = c.off;
-  return p;
+  p.partial = c.take((size_t)pr.batch * p.nblk * 4);
+  p.sumsq = c.take(init_sumsq_floats(pr.s, pr.batch) * 4);
+  p.scales = c.take((size_t)pr.batch * 4 * 4);
 }
 
-struct GramPlan {
-  Shape s;
-  int32_t nblk;
-  size_t xh[2], r, z, rz, q[2], partial, split, split_bytes, total;
-};
-
-GramPlan plan_gram(int64_t batch, int64_t rows, int64_t cols, int32_t cdt) {
-  GramPlan p;
-  p.s = canon(rows, cols);
-  p.nblk = norm_blocks(rows * cols);
+void plan_gram_regions(const Prob& pr, int32_t cdt, Carver& c, GramPlan& p) {
+  p.nblk = norm_blocks(pr.rows * pr.cols);
   const size_t cs = dt_size(cdt);
-  const size_t nm = (size_t)batch * p.s.np * p.s.mp, nn = (size_t)batch * p.s.np * p.s.np;
-  Carver c;
-  for (int i = 0; i < 2; ++i) {
-    p.xh[i] = c.take(nm * cs);
-  }
+  const size_t nm = (size_t)pr.batch * pr.s.np * pr.s.mp, nn = (size_t)pr.batch * pr.s.np * pr.s.np;
+  for (int i = 0; i < 2; ++i) p.xh[i] = c.take(nm * cs);
   p.r = c.take(nn * cs);
   p.z = c.take(nn * cs);
   p.rz = c.take(nn * cs);
   p.q[0] = c.take(nn * cs);
   p.q[1] = c.take(nn * cs);
-  p.partial = c.take((size_t)batch * p.nblk * 4);
-  p.split_bytes = split_scratch(p.s, batch, cdt);
-  p.split = c.take(p.split_bytes);
-  p.total = c.off;
-  return p;
+  p.partial = c.take((size_t)pr.batch * p.nblk * 4);
+}
+
+// Every problem's regions, one after the other, then the K-split scratch.
+template <typename P, typename F>
+CallPlan<P> plan_call(const Prob* pr, int ng, int32_t cdt, F regions) {
+  CallPlan<P> cp;
+  cp.ng = ng;
+  Carver c;
+  for (int i = 0; i < ng; ++i) regions(pr[i], cdt, c, cp.p[i]);
+  cp.split_bytes = split_scratch(pr, ng, cdt);
+  cp.split = c.take(cp.split_bytes);
+  cp.total = c.off;
+  return cp;
 }
 
 // ---------------------------------------------------------------- timing --
@@ -224,28 +241,34 @@ int tri_blocks(int tiles) {
   return tv / 2 * (tv + 1);
 }
 
-// How one product launch is laid out: tile configuration, tiles, and the
-// K split of the tiles past the last full round of resident blocks.
-struct LaunchPlan {
-  int bm;  // tile edge: 256, 128 or 64
-  int32_t tiles_m, tiles_n, tpm;
-  int64_t nt, nfull, tail;
-  int32_t split;
-  size_t partial_bytes;
+// Sizes of one group of a product launch: C (M x N per matrix) over
+// `batch` matrices, K the padded contraction length.
+struct Dims {
+  int64_t M, N, K, batch;
 };
 
-LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri, int32_t cdt) {
-  LaunchPlan l;
-  auto tiles_at = [&](int64_t e) {
-    const int64_t tm = (M + e - 1) / e, t = tm * ((N + e - 1) / e);
-    return (tri ? (t + tm) / 2 : t) * batch;
+GroupPlan plan_groups(const Dims* d, int ng, bool tri, int32_t cdt) {
+  GroupPlan l;
+  std::memset(&l, 0, sizeof(l));
+  l.ng = ng;
+  for (int i = 0; i < ng; ++i) l.order[i] = i;
+  for (int i = 1; i < ng; ++i)  // stable: equal K keeps the caller's order
+    for (int j = i; j > 0 && d[l.order[j]].K > d[l.order[j - 1]].K; --j) std::swap(l.order[j], l.order[j - 1]);
+  auto tiles_at = [&](const Dims& x, int64_t e) {
+    const int64_t tm = (x.M + e - 1) / e, t = tm * ((x.N + e - 1) / e);
+    return (tri ? (t + tm) / 2 : t) * x.batch;
   };
+  int64_t t256 = 0, t128 = 0;
+  for (int i = 0; i < ng; ++i) {
+    t256 += tiles_at(d[i], 256);
+    t128 += tiles_at(d[i], 128);
+  }
+  const Dims& last = d[l.order[ng - 1]];  // shortest K
   // the largest tile that still gives every CU a tile; 64 x 64 tiles (one
   // wave) when even 128 x 128 tiles leave CUs idle
-  const int64_t kslices = K / (cdt == MSIGN_F32 ? 16 : 32);
-  const int64_t t256 = tiles_at(256);
+  const int64_t kslices = last.K / (cdt == MSIGN_F32 ? 16 : 32);
   bool big = t256 >= kCUs;
-  if (!big && t256 > 0 && K >= 2048) {
+  if (!big && t256 > 0 && last.K >= 2048) {
     // long K: a K split of the big tiles that fills most CUs beats smaller
     // tiles (which would leave some CUs with two long tiles)
     int64_t sp = kCUs / t256;
@@ -253,109 +276,126 @@ LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri,
     if (sp > kslices / 4) sp = kslices / 4;
     big = t256 * sp >= kCUs * 3 / 4;
   }
-  l.bm = big ? 256 : (tiles_at(128) >= kCUs ? 128 : 64);
+  l.bm = big ? 256 : (t128 >= kCUs ? 128 : 64);
   // Blocks per CU that splitting the last round aims for (measured): one
   // 16-wave block of 256 x 256 keeps a CU busy; 4-wave 128 x 128 blocks
   // gain from two per CU.  A 64 x 64 tile is already shared along K by its
   // four waves.
   const int per_cu = l.bm == 128 ? 2 : 1;
   const int kwaves = l.bm == 64 ? 4 : 1;
-  l.tiles_m = (int32_t)((M + l.bm - 1) / l.bm);
-  l.tiles_n = (int32_t)((N + l.bm - 1) / l.bm);
-  l.tpm = tri ? tri_blocks(l.tiles_m) : l.tiles_m * l.tiles_n;
-  l.nt = (int64_t)l.tpm * batch;
-  l.nfull = l.nt;
+  int64_t ntot = 0;
+  for (int i = 0; i < ng; ++i) {
+    l.tiles_m[i] = (int32_t)((d[i].M + l.bm - 1) / l.bm);
+    l.tiles_n[i] = (int32_t)((d[i].N + l.bm - 1) / l.bm);
+    l.tpm[i] = tri ? tri_blocks(l.tiles_m[i]) : l.tiles_m[i] * l.tiles_n[i];
+    l.nt[i] = (int64_t)l.tpm[i] * d[i].batch;
+    ntot += l.nt[i];
+  }
   l.tail = 0;
   l.split = 1;
   const int64_t slots = (int64_t)kCUs * per_cu;
-  const int64_t rem = l.nt % slots;
-  if (rem > 0) {
-    int64_t sp = slots / rem;
+  const int64_t rem = ntot % slots;
+  const int64_t nlast = l.nt[l.order[ng - 1]];
+  if (rem > 0 && nlast > 0) {
+    // the last round: rem tiles, of which the last group's are split into
+    // the slots the whole tiles before them leave free
+    const int64_t tail = rem < nlast ? rem : nlast;
+    int64_t sp = (slots - (rem - tail)) / tail;
     if (sp > kSplitMax) sp = kSplitMax;     // bounds the partial-sum traffic
     if (sp > kslices / (4 * kwaves)) sp = kslices / (4 * kwaves);  // >= 4 K slices per wave
     if (sp >= 2) {
       l.split = (int32_t)sp;
-      l.tail = rem;
-      l.nfull = l.nt - rem;
+      l.tail = tail;
     }
   }
   l.partial_bytes = (size_t)l.tail * l.split * l.bm * l.bm * 4;
   return l;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int BKB, int NST, bool TRI, int KW, bool AT>
-hipError_t launch_cfg(GemmParams q, const LaunchPlan& l, hipStream_t st) {
-  q.tiles_m = l.tiles_m;
-  q.tiles_n = l.tiles_n;
-  q.tpm = l.tpm;
-  q.nfull = (int32_t)l.nfull;
-  q.split = l.split;
-  const int64_t blocks = l.nfull + l.tail * l.split;
-  if (blocks == 0) return hipSuccess;
-  gemm_nt_kernel<T, BM, BN, WGM, WGN, BKB, NST, TRI, KW, AT>
-      <<<dim3((unsigned)blocks), WGM * WGN * KW * 64, 0, st>>>(q);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || l.tail == 0) return e;
-  gemm_nt_reduce_kernel<T, BM, BN, WGM, WGN, TRI>
-      <<<dim3((unsigned)(l.tail * WGM * WGN)), BM / WGM / 16 * 64, 0, st>>>(q);
-  return hipGetLastError();
+// The one-group view of a launch (workspace sizing of single problems).
+struct LaunchPlan {
+  int bm;
+  int32_t tiles_m, tiles_n, tpm;
+  int64_t nt, tail;
+  int32_t split;
+  size_t partial_bytes;
+};
+
+LaunchPlan plan_launch(int64_t M, int64_t N, int64_t K, int64_t batch, bool tri, int32_t cdt) {
+  const Dims d{M, N, K, batch};
+  const GroupPlan g = plan_groups(&d, 1, tri, cdt);
+  LaunchPlan l;
+  l.bm = g.bm;
+  l.tiles_m = g.tiles_m[0];
+  l.tiles_n = g.tiles_n[0];
+  l.tpm = g.tpm[0];
+  l.nt = g.nt[0];
+  l.tail = g.tail;
+  l.split = g.split;
+  l.partial_bytes = g.partial_bytes;
+  return l;
 }
 
-template <typename T, bool TRI>
-hipError_t launch_nt_t(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
-  static_assert(TRI, "rectangular products go through launch_nt_at");
-  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 0, TRI, 1, false>(q, l, st);
-  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 0, TRI, 1, false>(q, l, st);
-  return launch_cfg<T, 64, 64, 1, 1, 64, 2, TRI, 4, false>(q, l, st);
-}
+static_assert(kMaxGroups == MSIGN_MAX_GROUPS, "group table size");
 
-// Rectangular products with P stored K-major (the iterate X, n x m, read
-// as X^T).
-template <typename T>
-hipError_t launch_nt_at(const GemmParams& q, const LaunchPlan& l, hipStream_t st) {
-  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 0, false, 1, true>(q, l, st);
-  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 0, false, 1, true>(q, l, st);
-  return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, true>(q, l, st);
-}
-
-// Launch one product: a triangle product (both operands read along K, P == Q
-// symmetric or P Q^T symmetric) or a rectangular one with P stored K-major.
-// `partial`/`partial_cap` is workspace for the K-split tail; with too little
-// of it the tail is computed whole instead.
+// Launch one product over ng groups (1..MSIGN_MAX_GROUPS, each with its own
+// operands, sizes and batch): a triangle product (both operands read along
+// K, P == Q symmetric or P Q^T symmetric) or a rectangular one with P stored
+// K-major.  `partial`/`partial_cap` is workspace for the K-split tail; with
+// too little of it the tail is computed whole instead.
 enum ProductKind { TRIANGLE, RECT_KMAJOR };
 
-hipError_t launch_nt(int32_t cdt, ProductKind kind, GemmParams q, int64_t batch, hipStream_t st,
-                     void* partial = nullptr, size_t partial_cap = 0) {
+Dims dims_of(const GemmParams& q, int64_t batch) { return Dims{q.M, q.N, q.K, batch}; }
+
+hipError_t launch_grouped(int32_t cdt, ProductKind kind, GemmParams* qs, const int64_t* batches, int ng,
+                          hipStream_t st, void* partial, size_t partial_cap, GroupPlan* used = nullptr) {
   const bool tri = kind == TRIANGLE;
-  LaunchPlan l = plan_launch(q.M, q.N, q.K, batch, tri, cdt);
+  Dims d[MSIGN_MAX_GROUPS];
+  for (int i = 0; i < ng; ++i) d[i] = dims_of(qs[i], batches[i]);
+  GroupPlan l = plan_groups(d, ng, tri, cdt);
   if (l.tail > 0 && (partial == nullptr || partial_cap < l.partial_bytes)) {
-    l.nfull = l.nt;
     l.tail = 0;
     l.split = 1;
   }
-  q.partial = static_cast<float*>(partial);
-  switch (cdt) {
-    case MSIGN_BF16: return tri ? launch_nt_t<bf16_t, true>(q, l, st) : launch_nt_at<bf16_t>(q, l, st);
-    case MSIGN_F16: return tri ? launch_nt_t<f16_t, true>(q, l, st) : launch_nt_at<f16_t>(q, l, st);
-    default: return tri ? launch_nt_t<float, true>(q, l, st) : launch_nt_at<float>(q, l, st);
-  }
+  for (int i = 0; i < ng; ++i) qs[i].partial = static_cast<float*>(partial);
+  if (used) *used = l;
+  return ng == 1 ? launch_products_single(cdt, tri, qs, l, st) : launch_products_grouped(cdt, tri, qs, l, st);
+}
+
+hipError_t launch_nt(int32_t cdt, ProductKind kind, GemmParams q, int64_t batch, hipStream_t st,
+                     void* partial = nullptr, size_t partial_cap = 0) {
+  return launch_grouped(cdt, kind, &q, &batch, 1, st, partial, partial_cap);
 }
 
 // acc^2 slots (one per tile, wave and fragment row) of the A A launch.
 int32_t sumsq_slots_per_tile(int bm) { return bm == 256 ? 16 * 4 : (bm == 128 ? 4 * 4 : 4); }
 
-size_t init_sumsq_floats(const Shape& s, int64_t batch, int32_t cdt) {
-  const LaunchPlan l = plan_launch(s.np, s.np, s.np, batch, true, cdt);
-  return (size_t)l.nt * sumsq_slots_per_tile(l.bm);
+// Room for the acc^2 slots of an A A launch at any tile size (a grouped
+// launch may pick another tile size than the problem alone would).
+size_t init_sumsq_floats(const Shape& s, int64_t batch) {
+  size_t most = 0;
+  for (int bm = 64; bm <= 256; bm *= 2) {
+    const size_t n = (size_t)tri_blocks((int)((s.np + bm - 1) / bm)) * batch * sumsq_slots_per_tile(bm);
+    most = n > most ? n : most;
+  }
+  return most;
 }
 
-// Largest K-split scratch any product of an NS or Gram call needs.
-size_t split_scratch(const Shape& s, int64_t batch, int32_t cdt) {
+// Largest K-split scratch any product of an NS or Gram call over these
+// problems needs (X X^T, the n x n products and the update).
+size_t split_scratch(const Prob* pr, int ng, int32_t cdt) {
+  Dims d[3][MSIGN_MAX_GROUPS];
+  for (int i = 0; i < ng; ++i) {
+    const Shape& s = pr[i].s;
+    d[0][i] = Dims{s.np, s.np, s.mp, pr[i].batch};
+    d[1][i] = Dims{s.np, s.np, s.np, pr[i].batch};
+    d[2][i] = Dims{s.mp, s.np, s.np, pr[i].batch};
+  }
   size_t b = 0;
-  const LaunchPlan ls[3] = {plan_launch(s.np, s.np, s.mp, batch, true, cdt),
-                            plan_launch(s.np, s.np, s.np, batch, true, cdt),
-                            plan_launch(s.mp, s.np, s.np, batch, false, cdt)};
-  for (const LaunchPlan& l : ls) b = l.partial_bytes > b ? l.partial_bytes : b;
+  for (int k = 0; k < 3; ++k) {
+    const size_t v = plan_groups(d[k], ng, k < 2, cdt).partial_bytes;
+    b = v > b ? v : b;
+  }
   return b;
 }
 
@@ -491,77 +531,131 @@ void add_final_out(GemmParams& g, void* y, const Shape& s, int32_t io_dtype) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-size_t msign_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t compute_dtype) {
-  if (batch < 0 || rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim || batch > kMaxBatch ||
-      !dt_valid(compute_dtype))
-    return (size_t)-1;
-  if (batch == 0 || rows == 0 || cols == 0) return 0;
-  return plan_ns(batch, rows, cols, compute_dtype).total;
+// Non-empty problems of a call, checked one by one; `*ng` of them.
+msign_status_t gather(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t cdt,
+                      int32_t steps, const float* coeffs, float eps, Prob* pr, int* ng) {
+  *ng = 0;
+  if (ngroups < 1 || ngroups > MSIGN_MAX_GROUPS)
+    return fail(MSIGN_ERR_ARG, "ngroups must be in 1.." + std::to_string(MSIGN_MAX_GROUPS));
+  if (!groups) return fail(MSIGN_ERR_ARG, "groups must be non-null");
+  for (int i = 0; i < ngroups; ++i) {
+    const msign_group_t& g = groups[i];
+    bool empty = false;
+    msign_status_t st = check_common(g.x, g.y, g.batch, g.rows, g.cols, io_dtype, cdt, steps, coeffs, eps, &empty);
+    if (st != MSIGN_OK) return ngroups > 1 ? fail(st, "group " + std::to_string(i) + ": " + g_err) : st;
+    if (empty) continue;
+    Prob& p = pr[(*ng)++];
+    p.x = g.x; p.y = g.y; p.batch = g.batch; p.rows = g.rows; p.cols = g.cols;
+    p.s = canon(g.rows, g.cols);
+  }
+  return MSIGN_OK;
 }
 
-size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t compute_dtype) {
-  if (batch < 0 || rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim || batch > kMaxBatch ||
-      !dt_valid(compute_dtype))
-    return (size_t)-1;
-  if (batch == 0 || rows == 0 || cols == 0) return 0;
-  return plan_gram(batch, rows, cols, compute_dtype).total;
+// Workspace size and alignment, no input or output inside it, y == x or
+// apart within a problem, and no problem's output overlapping another
+// problem's input or output.
+msign_status_t check_call_ws(const Prob* pr, int ng, int32_t io_dtype, void* ws, size_t ws_bytes, size_t need) {
+  const size_t es = dt_size(io_dtype);
+  for (int i = 0; i < ng; ++i) {
+    const size_t bi = (size_t)pr[i].batch * pr[i].rows * pr[i].cols * es;
+    msign_status_t st = check_ws_alias(pr[i].x, pr[i].y, bi, ws, ws_bytes, need);
+    if (st != MSIGN_OK) return st;
+    for (int j = 0; j < ng; ++j) {
+      if (j == i) continue;
+      const size_t bj = (size_t)pr[j].batch * pr[j].rows * pr[j].cols * es;
+      if (overlap(pr[i].y, bi, pr[j].x, bj) || overlap(pr[i].y, bi, pr[j].y, bj))
+        return fail(MSIGN_ERR_ALIAS, "the output of one group overlaps the input or output of another");
+    }
+  }
+  return MSIGN_OK;
 }
 
-msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
-                        int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
-                        float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return msign_ns_ex(x, y, batch, rows, cols, io_dtype, compute_dtype, steps, coeffs, eps, 0u, workspace,
-                     workspace_bytes, stream);
+size_t call_workspace(const msign_group_t* groups, int32_t ngroups, int32_t cdt, bool gram) {
+  if (ngroups < 1 || ngroups > MSIGN_MAX_GROUPS || !groups || !dt_valid(cdt)) return (size_t)-1;
+  Prob pr[MSIGN_MAX_GROUPS];
+  int ng = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    const msign_group_t& g = groups[i];
+    if (g.batch < 0 || g.rows < 0 || g.cols < 0 || g.rows > kMaxDim || g.cols > kMaxDim || g.batch > kMaxBatch)
+      return (size_t)-1;
+    if (g.batch == 0 || g.rows == 0 || g.cols == 0) continue;
+    Prob& p = pr[ng++];
+    p.batch = g.batch; p.rows = g.rows; p.cols = g.cols;
+    p.s = canon(g.rows, g.cols);
+  }
+  if (ng == 0) return 0;
+  return gram ? plan_call<GramPlan>(pr, ng, cdt, plan_gram_regions).total
+              : plan_call<NsPlan>(pr, ng, cdt, plan_ns_regions).total;
 }
 
-msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
-                           int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
-                           float eps, uint32_t flags, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+// Standard NS over ng problems: every product is one launch over all of
+// them (a grouped launch), the normalise passes run per problem.
+msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
+                      int32_t steps, const float* coeffs, float eps, uint32_t flags, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
   if (flags & ~(uint32_t)MSIGN_NS_IMPROVED_INIT) return fail(MSIGN_ERR_ARG, "unknown flag");
   const bool improved = (flags & MSIGN_NS_IMPROVED_INIT) != 0;
-  bool empty = false;
-  msign_status_t st = check_common(x, y, batch, rows, cols, io_dtype, compute_dtype, steps, coeffs, eps, &empty);
-  if (st != MSIGN_OK || empty) return st;
-  const NsPlan pl = plan_ns(batch, rows, cols, compute_dtype);
-  const size_t io_bytes = (size_t)batch * rows * cols * dt_size(io_dtype);
-  st = check_ws_alias(x, y, io_bytes, workspace, workspace_bytes, pl.total);
+  Prob pr[MSIGN_MAX_GROUPS];
+  int ng = 0;
+  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+  if (st != MSIGN_OK || ng == 0) return st;
+  const CallPlan<NsPlan> cp = plan_call<NsPlan>(pr, ng, compute_dtype, plan_ns_regions);
+  st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, cp.total);
   if (st != MSIGN_OK) return st;
 
-  const Shape& s = pl.s;
   const int32_t cdt = compute_dtype;
-  const int64_t nm = s.np * s.mp, nn = s.np * s.np;
-  void* x32[2] = {at(workspace, pl.x32[0]), at(workspace, pl.x32[1])};
-  void* xh[2] = {at(workspace, pl.xh[0]), at(workspace, pl.xh[1])};
-  void* A = at(workspace, pl.a);
-  void* B = at(workspace, pl.b);
-  float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
-  float* sumsq = reinterpret_cast<float*>(at(workspace, pl.sumsq));
-  float* scales = reinterpret_cast<float*>(at(workspace, pl.scales));
-  void* split = at(workspace, pl.split);
+  void* split = at(workspace, cp.split);
+  struct G {
+    Shape s;
+    int64_t nm, nn;
+    void *x32[2], *xh[2], *A, *B;
+    float *partial, *sumsq, *scales;
+  } gv[MSIGN_MAX_GROUPS];
+  int64_t batches[MSIGN_MAX_GROUPS];
+  for (int i = 0; i < ng; ++i) {
+    const NsPlan& pl = cp.p[i];
+    G& v = gv[i];
+    v.s = pr[i].s;
+    v.nm = v.s.np * v.s.mp;
+    v.nn = v.s.np * v.s.np;
+    for (int k = 0; k < 2; ++k) {
+      v.x32[k] = at(workspace, pl.x32[k]);
+      v.xh[k] = at(workspace, pl.xh[k]);
+    }
+    v.A = at(workspace, pl.a);
+    v.B = at(workspace, pl.b);
+    v.partial = reinterpret_cast<float*>(at(workspace, pl.partial));
+    v.sumsq = reinterpret_cast<float*>(at(workspace, pl.sumsq));
+    v.scales = reinterpret_cast<float*>(at(workspace, pl.scales));
+    batches[i] = pr[i].batch;
+    // X0 (n x m): in the compute dtype (the X X^T operand, also read
+    // K-major as X^T by the update) and the fp32 master
+    NormOut outs[2] = {
+        {v.xh[0], v.s.mp, v.nm, cdt, 0},
+        {v.x32[0], v.s.mp, v.nm, MSIGN_F32, 0},
+    };
+    st = launch_normalize(pr[i].x, io_dtype, pr[i].batch, pr[i].rows, pr[i].cols, v.s, v.partial, pl.nblk, eps,
+                          outs, 2, stream);
+    if (st != MSIGN_OK) return st;
+  }
 
-  // X0 (n x m): in the compute dtype (the X X^T operand, also read K-major
-  // as X^T by the update) and the fp32 master
-  NormOut outs[2] = {
-      {xh[0], s.mp, nm, cdt, 0},
-      {x32[0], s.mp, nm, MSIGN_F32, 0},
-  };
-  st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 2, stream);
-  if (st != MSIGN_OK) return st;
-
+  GemmParams qs[MSIGN_MAX_GROUPS];
   for (int t = 0; t < steps; ++t) {
     float a, b, c;
     coeff_at(coeffs, t, &a, &b, &c);
     const int cur = t & 1, nxt = cur ^ 1;
     hipError_t e;
     {  // A = X X^T
-      GemmParams g = gemm_base(xh[cur], s.mp, nm, xh[cur], s.mp, nm, s.np, s.np, s.mp, 1.f);
-      add_out(g, A, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
+      for (int i = 0; i < ng; ++i) {
+        const G& v = gv[i];
+        qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
+        add_out(qs[i], v.A, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+      }
       TimedLaunch tl(KC_SYRK, stream);
-      e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
+      e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "X X^T");
     }
     // Improved initial normalisation (§改良初值), first step only: A2 = A A
@@ -569,66 +663,79 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, 
     // and the update below scaled by 1/s.
     const bool rescale = improved && t == 0;
     if (rescale) {
-      GemmParams g = gemm_base(A, s.np, nn, A, s.np, nn, s.np, s.np, s.np, 1.f);
-      add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
-      g.sumsq = sumsq;
+      for (int i = 0; i < ng; ++i) {
+        const G& v = gv[i];
+        qs[i] = gemm_base(v.A, v.s.np, v.nn, v.A, v.s.np, v.nn, v.s.np, v.s.np, v.s.np, 1.f);
+        add_out(qs[i], v.B, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+        qs[i].sumsq = v.sumsq;
+      }
+      GroupPlan used;
       {
         TimedLaunch tl(KC_SQUARE, stream);
-        e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
+        e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes, &used);
         if (e != hipSuccess) return hip_fail(e, "A A (first step)");
       }
-      const LaunchPlan l = plan_launch(s.np, s.np, s.np, batch, true, cdt);
-      g.tiles_m = l.tiles_m;
-      g.tiles_n = l.tiles_n;
-      g.tpm = l.tpm;
-      TimedLaunch tl(KC_NORM, stream);
-      init_scale_kernel<<<dim3((unsigned)batch), 256, 0, stream>>>(g, sumsq_slots_per_tile(l.bm), eps, scales);
-      e = hipGetLastError();
-      if (e != hipSuccess) return hip_fail(e, "init_scale_kernel");
-      const unsigned nb = (unsigned)((nn / 4 + 255) / 256);
-      init_combine_kernel<<<dim3(nb, (unsigned)batch), 256, 0, stream>>>(A, B, nn, cdt, b, c, scales);
-      e = hipGetLastError();
-      if (e != hipSuccess) return hip_fail(e, "init_combine_kernel");
+      for (int i = 0; i < ng; ++i) {
+        const G& v = gv[i];
+        GemmParams q = qs[i];
+        q.tiles_m = used.tiles_m[i];
+        q.tiles_n = used.tiles_n[i];
+        q.tpm = used.tpm[i];
+        TimedLaunch tl(KC_NORM, stream);
+        init_scale_kernel<<<dim3((unsigned)pr[i].batch), 256, 0, stream>>>(q, sumsq_slots_per_tile(used.bm), eps,
+                                                                           v.scales);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "init_scale_kernel");
+        const unsigned nb = (unsigned)((v.nn / 4 + 255) / 256);
+        init_combine_kernel<<<dim3(nb, (unsigned)pr[i].batch), 256, 0, stream>>>(v.A, v.B, v.nn, cdt, b, c,
+                                                                                  v.scales);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "init_combine_kernel");
+      }
     }
     // A cubic step (c = 0, "msign算子的Newton-Schulz迭代（上）" §迭代计算) has
     // B = b A: no A A product, and the next product takes A scaled by b.
     const bool cubic = (c == 0.f) && !rescale;
     if (!cubic && !rescale) {  // B = c A A + b A
-      GemmParams g = gemm_base(A, s.np, nn, A, s.np, nn, s.np, s.np, s.np, c);
-      set_d(g, A, s.np, nn, cdt, b, true);
-      add_out(g, B, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
+      for (int i = 0; i < ng; ++i) {
+        const G& v = gv[i];
+        qs[i] = gemm_base(v.A, v.s.np, v.nn, v.A, v.s.np, v.nn, v.s.np, v.s.np, v.s.np, c);
+        set_d(qs[i], v.A, v.s.np, v.nn, cdt, b, true);
+        add_out(qs[i], v.B, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+      }
       TimedLaunch tl(KC_SQUARE, stream);
-      e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
+      e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "c A A + b A");
     }
     {  // X' = B X + a X, as C' = X^T B + a X^T (m x n) with X read K-major;
        // C'[i][j] is stored at X'[j][i], four consecutive i per store
-      GemmParams g = gemm_base(xh[cur], s.mp, nm, cubic ? A : B, s.np, nn, s.mp, s.np, s.np,
-                               cubic ? b : 1.f);
-      if (rescale) g.vscale = scales;
-      set_d(g, x32[cur], s.mp, nm, MSIGN_F32, a, true);
-      if (t + 1 < steps) {
-        add_out(g, x32[nxt], s.mp, nm, MSIGN_F32, true, s.mp, s.np, 0.f, 0, true);
-        add_out(g, xh[nxt], s.mp, nm, cdt, true, s.mp, s.np, 0.f, 0, true);
-      } else {
-        add_final_out(g, y, s, io_dtype);
+      for (int i = 0; i < ng; ++i) {
+        const G& v = gv[i];
+        GemmParams& g = qs[i];
+        g = gemm_base(v.xh[cur], v.s.mp, v.nm, cubic ? v.A : v.B, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np,
+                      cubic ? b : 1.f);
+        if (rescale) g.vscale = v.scales;
+        set_d(g, v.x32[cur], v.s.mp, v.nm, MSIGN_F32, a, true);
+        if (t + 1 < steps) {
+          add_out(g, v.x32[nxt], v.s.mp, v.nm, MSIGN_F32, true, v.s.mp, v.s.np, 0.f, 0, true);
+          add_out(g, v.xh[nxt], v.s.mp, v.nm, cdt, true, v.s.mp, v.s.np, 0.f, 0, true);
+        } else {
+          add_final_out(g, pr[i].y, v.s, io_dtype);
+        }
       }
       TimedLaunch tl(KC_RECT, stream);
-      e = launch_nt(cdt, RECT_KMAJOR, g, batch, stream, split, pl.split_bytes);
+      e = launch_grouped(cdt, RECT_KMAJOR, qs, batches, ng, stream, split, cp.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "B X + a X");
     }
   }
   return MSIGN_OK;
 }
 
-msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
-                             int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
-                             float eps, const int32_t* restart_after, int32_t n_restarts, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
+// Restart list of Gram NS: strictly increasing step indices in 1..steps-1
+// (steps itself is checked with the other arguments).
+msign_status_t parse_restarts(int32_t steps, const int32_t* restart_after, int32_t n_restarts, bool* restart_at) {
   if (n_restarts < 0 || (n_restarts > 0 && !restart_after) || (n_restarts == 0 && restart_after))
     return fail(MSIGN_ERR_ARG, "restart_after must be non-null exactly when n_restarts > 0");
-  bool restart_at[MSIGN_MAX_STEPS + 1] = {false};
   if (steps >= 1 && steps <= MSIGN_MAX_STEPS) {
     int prev = 0;
     for (int i = 0; i < n_restarts; ++i) {
@@ -639,50 +746,95 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
       prev = r;
     }
   }
-  bool empty = false;
-  msign_status_t st = check_common(x, y, batch, rows, cols, io_dtype, compute_dtype, steps, coeffs, eps, &empty);
-  if (st != MSIGN_OK || empty) return st;
-  const GramPlan pl = plan_gram(batch, rows, cols, compute_dtype);
-  const size_t io_bytes = (size_t)batch * rows * cols * dt_size(io_dtype);
-  st = check_ws_alias(x, y, io_bytes, workspace, workspace_bytes, pl.total);
+  return MSIGN_OK;
+}
+
+// Gram NS over ng problems, every product one grouped launch.
+msign_status_t gram_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
+                        int32_t steps, const float* coeffs, float eps, const int32_t* restart_after,
+                        int32_t n_restarts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  bool restart_at[MSIGN_MAX_STEPS + 1] = {false};
+  msign_status_t st0 = parse_restarts(steps, restart_after, n_restarts, restart_at);
+  if (st0 != MSIGN_OK) return st0;
+  Prob pr[MSIGN_MAX_GROUPS];
+  int ng = 0;
+  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+  if (st != MSIGN_OK || ng == 0) return st;
+  const CallPlan<GramPlan> cp = plan_call<GramPlan>(pr, ng, compute_dtype, plan_gram_regions);
+  st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, cp.total);
   if (st != MSIGN_OK) return st;
 
-  const Shape& s = pl.s;
   const int32_t cdt = compute_dtype;
-  const int64_t nm = s.np * s.mp, nn = s.np * s.np;
-  void* xh[2] = {at(workspace, pl.xh[0]), at(workspace, pl.xh[1])};
-  void* R = at(workspace, pl.r);
-  void* Z = at(workspace, pl.z);
-  void* RZ = at(workspace, pl.rz);
-  void* Qb[2] = {at(workspace, pl.q[0]), at(workspace, pl.q[1])};
-  float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
-  void* split = at(workspace, pl.split);
-
-  NormOut outs[1] = {{xh[0], s.mp, nm, cdt, 0}};
-  st = launch_normalize(x, io_dtype, batch, rows, cols, s, partial, pl.nblk, eps, outs, 1, stream);
-  if (st != MSIGN_OK) return st;
+  void* split = at(workspace, cp.split);
+  struct G {
+    Shape s;
+    int64_t nm, nn;
+    void *xh[2], *R, *Z, *RZ, *Qb0, *Qb1;  // Q double-buffered
+  } gv[MSIGN_MAX_GROUPS];
+  int64_t batches[MSIGN_MAX_GROUPS];
+  for (int i = 0; i < ng; ++i) {
+    const GramPlan& pl = cp.p[i];
+    G& v = gv[i];
+    v.s = pr[i].s;
+    v.nm = v.s.np * v.s.mp;
+    v.nn = v.s.np * v.s.np;
+    v.xh[0] = at(workspace, pl.xh[0]);
+    v.xh[1] = at(workspace, pl.xh[1]);
+    v.R = at(workspace, pl.r);
+    v.Z = at(workspace, pl.z);
+    v.RZ = at(workspace, pl.rz);
+    v.Qb0 = at(workspace, pl.q[0]);
+    v.Qb1 = at(workspace, pl.q[1]);
+    batches[i] = pr[i].batch;
+    NormOut outs[1] = {{v.xh[0], v.s.mp, v.nm, cdt, 0}};
+    st = launch_normalize(pr[i].x, io_dtype, pr[i].batch, pr[i].rows, pr[i].cols, v.s,
+                          reinterpret_cast<float*>(at(workspace, pl.partial)), pl.nblk, eps, outs, 1, stream);
+    if (st != MSIGN_OK) return st;
+  }
 
   hipError_t e;
   int cur = 0, qc = 0;
+  GemmParams qs[MSIGN_MAX_GROUPS];
   auto gram_xxt = [&]() -> msign_status_t {
-    GemmParams g = gemm_base(xh[cur], s.mp, nm, xh[cur], s.mp, nm, s.np, s.np, s.mp, 1.f);
-    add_out(g, R, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
+    for (int i = 0; i < ng; ++i) {
+      const G& v = gv[i];
+      qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
+      add_out(qs[i], v.R, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+    }
     TimedLaunch tl(KC_SYRK, stream);
-    e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
+    e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes);
     return e == hipSuccess ? MSIGN_OK : hip_fail(e, "R = X X^T");
   };
-  // tri product: out = P Q^T + beta D  (all n x n, symmetric)
-  auto square = [&](const void* P, const void* Q, float alpha, const void* D, float beta, void* out,
-                    void* out2, float diag2, const char* what) -> msign_status_t {
-    GemmParams g = gemm_base(P, s.np, nn, Q, s.np, nn, s.np, s.np, s.np, alpha);
-    if (D) set_d(g, D, s.np, nn, cdt, beta, true);
-    add_out(g, out, s.np, nn, cdt, false, s.np, s.np, 0.f, 0, true);
-    if (out2) add_out(g, out2, s.np, nn, cdt, false, s.np, s.np, diag2, s.n, true);
+  // tri product: out = P Q^T + beta D  (all n x n, symmetric); operands
+  // named by their member in G
+  using Buf = void* G::*;
+  auto square = [&](Buf P, Buf Q, float alpha, Buf D, float beta, Buf out, Buf out2, float diag2,
+                    const char* what) -> msign_status_t {
+    for (int i = 0; i < ng; ++i) {
+      G& v = gv[i];
+      qs[i] = gemm_base(v.*P, v.s.np, v.nn, v.*Q, v.s.np, v.nn, v.s.np, v.s.np, v.s.np, alpha);
+      if (D) set_d(qs[i], v.*D, v.s.np, v.nn, cdt, beta, true);
+      add_out(qs[i], v.*out, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+      if (out2) add_out(qs[i], v.*out2, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, diag2, v.s.n, true);
+    }
     TimedLaunch tl(KC_SQUARE, stream);
-    e = launch_nt(cdt, TRIANGLE, g, batch, stream, split, pl.split_bytes);
+    e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes);
     return e == hipSuccess ? MSIGN_OK : hip_fail(e, what);
   };
-
+  // rect product: C' = X^T Q (Q symmetric, X read K-major), stored
+  // transposed into the other X, or into y on the last one
+  auto apply_q = [&](bool final_out, const char* what) -> msign_status_t {
+    for (int i = 0; i < ng; ++i) {
+      G& v = gv[i];
+      qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, qc ? v.Qb1 : v.Qb0, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np, 1.f);
+      if (final_out) add_final_out(qs[i], pr[i].y, v.s, io_dtype);
+      else add_out(qs[i], v.xh[cur ^ 1], v.s.mp, v.nm, cdt, true, v.s.mp, v.s.np, 0.f, 0, true);
+    }
+    TimedLaunch tl(KC_RECT, stream);
+    e = launch_grouped(cdt, RECT_KMAJOR, qs, batches, ng, stream, split, cp.split_bytes);
+    return e == hipSuccess ? MSIGN_OK : hip_fail(e, what);
+  };
   st = gram_xxt();
   if (st != MSIGN_OK) return st;
   bool fresh = true;  // Q == I
@@ -691,43 +843,258 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows
     coeff_at(coeffs, t - 1, &a, &b, &c);
     const bool block_end = (t == steps) || restart_at[t];
     // Z = c R R + b R; on the first step of a block also Q = Z + a I
-    st = square(R, R, c, R, b, Z, fresh ? Qb[qc] : nullptr, a, "Z = b R + c R^2");
+    st = square(&G::R, &G::R, c, &G::R, b, &G::Z, fresh ? (qc ? &G::Qb1 : &G::Qb0) : nullptr, a,
+                "Z = b R + c R^2");
     if (st != MSIGN_OK) return st;
     if (!fresh) {  // Q <- Q Z + a Q
-      st = square(Qb[qc], Z, 1.f, Qb[qc], a, Qb[qc ^ 1], nullptr, 0.f, "Q <- Q Z + a Q");
+      const Buf q0 = qc ? &G::Qb1 : &G::Qb0, q1 = qc ? &G::Qb0 : &G::Qb1;
+      st = square(q0, &G::Z, 1.f, q0, a, q1, nullptr, 0.f, "Q <- Q Z + a Q");
       if (st != MSIGN_OK) return st;
       qc ^= 1;
     }
     fresh = false;
     if (!block_end) {
-      st = square(R, Z, 1.f, R, a, RZ, nullptr, 0.f, "RZ <- R Z + a R");
+      st = square(&G::R, &G::Z, 1.f, &G::R, a, &G::RZ, nullptr, 0.f, "RZ <- R Z + a R");
       if (st != MSIGN_OK) return st;
-      st = square(Z, RZ, 1.f, RZ, a, R, nullptr, 0.f, "R <- Z RZ + a RZ");
+      st = square(&G::Z, &G::RZ, 1.f, &G::RZ, a, &G::R, nullptr, 0.f, "R <- Z RZ + a RZ");
       if (st != MSIGN_OK) return st;
     }
     if (restart_at[t]) {  // X <- Q X, R = X X^T, Q = I
-      // as C' = X^T Q (Q symmetric), stored transposed into the other X
-      GemmParams g = gemm_base(xh[cur], s.mp, nm, Qb[qc], s.np, nn, s.mp, s.np, s.np, 1.f);
-      add_out(g, xh[cur ^ 1], s.mp, nm, cdt, true, s.mp, s.np, 0.f, 0, true);
-      {
-        TimedLaunch tl(KC_RECT, stream);
-        e = launch_nt(cdt, RECT_KMAJOR, g, batch, stream, split, pl.split_bytes);
-        if (e != hipSuccess) return hip_fail(e, "restart X <- Q X");
-      }
+      st = apply_q(false, "restart X <- Q X");
+      if (st != MSIGN_OK) return st;
       cur ^= 1;
       st = gram_xxt();
       if (st != MSIGN_OK) return st;
       fresh = true;
     }
   }
-  {  // y = Q X
-    GemmParams g = gemm_base(xh[cur], s.mp, nm, Qb[qc], s.np, nn, s.mp, s.np, s.np, 1.f);
-    add_final_out(g, y, s, io_dtype);
-    TimedLaunch tl(KC_RECT, stream);
-    e = launch_nt(cdt, RECT_KMAJOR, g, batch, stream, split, pl.split_bytes);
-    if (e != hipSuccess) return hip_fail(e, "y = Q X");
+  return apply_q(true, "y = Q X");  // y = Q X
+}
+
+// ------------------------------------------------------------ Muon step --
+
+// msign groups of a Muon step: x = the momentum (fp32), y = the fp32
+// update direction in the step's workspace (at offsets o_off[i]).
+struct MuonCall {
+  int ng;
+  msign_group_t mg[MSIGN_MAX_GROUPS];
+  const muon_group_t* src[MSIGN_MAX_GROUPS];
+  size_t o_off[MSIGN_MAX_GROUPS];
+  size_t msign_off, total;
+};
+
+bool muon_shape_ok(const muon_group_t& g) {
+  return g.batch >= 0 && g.rows >= 0 && g.cols >= 0 && g.rows <= kMaxDim && g.cols <= kMaxDim &&
+         g.batch <= kMaxBatch;
+}
+
+// Plans the workspace; the msign groups' pointers are those of `ws` (null
+// for a size query).
+msign_status_t plan_muon(const muon_group_t* groups, int32_t ngroups, int32_t method, int32_t cdt, void* ws,
+                         MuonCall* mc) {
+  mc->ng = 0;
+  if (ngroups < 1 || ngroups > MSIGN_MAX_GROUPS)
+    return fail(MSIGN_ERR_ARG, "ngroups must be in 1.." + std::to_string(MSIGN_MAX_GROUPS));
+  if (!groups) return fail(MSIGN_ERR_ARG, "groups must be non-null");
+  if (method != MUON_NS && method != MUON_GRAM) return fail(MSIGN_ERR_ARG, "method must be MUON_NS or MUON_GRAM");
+  if (!dt_valid(cdt)) return fail(MSIGN_ERR_DTYPE, "compute_dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
+  Carver c;
+  for (int i = 0; i < ngroups; ++i) {
+    const muon_group_t& g = groups[i];
+    if (!muon_shape_ok(g)) return fail(MSIGN_ERR_SHAPE, "group " + std::to_string(i) + ": invalid shape");
+    if (g.batch == 0 || g.rows == 0 || g.cols == 0) continue;
+    const int k = mc->ng++;
+    mc->src[k] = &g;
+    mc->o_off[k] = c.take((size_t)g.batch * g.rows * g.cols * 4);
+  }
+  mc->msign_off = c.off;
+  for (int k = 0; k < mc->ng; ++k) {
+    const muon_group_t& g = *mc->src[k];
+    mc->mg[k].x = g.m;
+    mc->mg[k].y = ws ? at(ws, mc->o_off[k]) : nullptr;
+    mc->mg[k].batch = g.batch;
+    mc->mg[k].rows = g.rows;
+    mc->mg[k].cols = g.cols;
+  }
+  const size_t need = mc->ng == 0 ? 0 : call_workspace(mc->mg, mc->ng, cdt, method == MUON_GRAM);
+  if (need == (size_t)-1) return fail(MSIGN_ERR_SHAPE, "invalid sizes");
+  mc->total = mc->ng == 0 ? 0 : mc->msign_off + need;
+  return MSIGN_OK;
+}
+
+unsigned elementwise_blocks(int64_t n) {
+  int64_t b = (n + 1023) / 1024;
+  if (b > 4096) b = 4096;
+  return (unsigned)(b < 1 ? 1 : b);
+}
+
+msign_status_t muon_run(const muon_group_t* groups, int32_t ngroups, int32_t io_dtype, float mu, float lr,
+                        int32_t method, int32_t compute_dtype, int32_t steps, const float* coeffs, float eps,
+                        uint32_t flags, const int32_t* restart_after, int32_t n_restarts, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!dt_valid(io_dtype)) return fail(MSIGN_ERR_DTYPE, "io_dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
+  if (!std::isfinite(mu) || !std::isfinite(lr)) return fail(MSIGN_ERR_ARG, "mu and lr must be finite");
+  if (method == MUON_GRAM && flags != 0) return fail(MSIGN_ERR_ARG, "flags apply to MUON_NS only");
+  if (flags & ~(uint32_t)MSIGN_NS_IMPROVED_INIT) return fail(MSIGN_ERR_ARG, "unknown flag");
+  if (method == MUON_GRAM) {
+    bool restart_at[MSIGN_MAX_STEPS + 1] = {false};
+    msign_status_t st0 = parse_restarts(steps, restart_after, n_restarts, restart_at);
+    if (st0 != MSIGN_OK) return st0;
+  }
+  MuonCall mc;
+  msign_status_t st = plan_muon(groups, ngroups, method, compute_dtype, workspace, &mc);
+  if (st != MSIGN_OK || mc.ng == 0) return st;
+  if (!workspace || workspace_bytes < mc.total)
+    return fail(MSIGN_ERR_WORKSPACE, "workspace is null or smaller than the required " + std::to_string(mc.total) + " bytes");
+  if (!aligned(workspace, 256)) return fail(MSIGN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t es = dt_size(io_dtype);
+  for (int k = 0; k < mc.ng; ++k) {
+    const muon_group_t& g = *mc.src[k];
+    if (!g.w || !g.g || !g.m) return fail(MSIGN_ERR_ARG, "w, g and m must be non-null");
+    if (!aligned(g.w, es) || !aligned(g.g, es) || !aligned(g.m, 4))
+      return fail(MSIGN_ERR_ARG, "w, g and m must be aligned to their element size");
+  }
+  {  // the msign call's own checks, before anything is launched
+    Prob pr[MSIGN_MAX_GROUPS];
+    int ng = 0;
+    st = gather(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, pr, &ng);
+    if (st != MSIGN_OK) return st;
+  }
+  // buffers: w and m written, g read; none may overlap the workspace, and a
+  // written buffer may overlap no other buffer
+  struct Buf { const void* p; size_t n; bool written; };
+  Buf bufs[3 * MSIGN_MAX_GROUPS];
+  int nb = 0;
+  for (int k = 0; k < mc.ng; ++k) {
+    const muon_group_t& g = *mc.src[k];
+    const size_t cnt = (size_t)g.batch * g.rows * g.cols;
+    bufs[nb++] = {g.w, cnt * es, true};
+    bufs[nb++] = {g.g, cnt * es, false};
+    bufs[nb++] = {g.m, cnt * 4, true};
+  }
+  for (int i = 0; i < nb; ++i) {
+    if (overlap(bufs[i].p, bufs[i].n, workspace, mc.total))
+      return fail(MSIGN_ERR_ALIAS, "w, g or m overlaps the workspace");
+    for (int j = 0; j < nb; ++j)
+      if (j != i && (bufs[i].written || bufs[j].written) && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(MSIGN_ERR_ALIAS, "w or m overlaps another buffer of the step");
+  }
+  // M <- mu M + G
+  for (int k = 0; k < mc.ng; ++k) {
+    const muon_group_t& g = *mc.src[k];
+    const int64_t n = g.batch * g.rows * g.cols;
+    const int32_t vec = aligned(g.m, 16) && aligned(g.g, 4 * es) ? 1 : 0;
+    TimedLaunch tl(KC_NORM, stream);
+    momentum_kernel<<<elementwise_blocks(n), 256, 0, stream>>>(g.m, g.g, io_dtype, n, mu, vec);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "momentum_kernel");
+  }
+  // O = msign(M), fp32, into the workspace
+  void* ms_ws = at(workspace, mc.msign_off);
+  const size_t ms_bytes = workspace_bytes - mc.msign_off;
+  st = method == MUON_NS
+           ? ns_run(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, flags, ms_ws, ms_bytes, stream)
+           : gram_run(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, restart_after, n_restarts, ms_ws,
+                      ms_bytes, stream);
+  if (st != MSIGN_OK) return st;
+  // W <- W - lr O
+  for (int k = 0; k < mc.ng; ++k) {
+    const muon_group_t& g = *mc.src[k];
+    const int64_t n = g.batch * g.rows * g.cols;
+    const float* o = reinterpret_cast<const float*>(at(workspace, mc.o_off[k]));
+    const int32_t vec = aligned(g.w, 4 * es) ? 1 : 0;
+    TimedLaunch tl(KC_NORM, stream);
+    update_kernel<<<elementwise_blocks(n), 256, 0, stream>>>(g.w, io_dtype, o, n, lr, vec);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "update_kernel");
   }
   return MSIGN_OK;
+}
+
+msign_group_t one_group(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols) {
+  msign_group_t g;
+  g.x = x; g.y = y; g.batch = batch; g.rows = rows; g.cols = cols;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t msign_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t compute_dtype) {
+  const msign_group_t g = one_group(nullptr, nullptr, batch, rows, cols);
+  return call_workspace(&g, 1, compute_dtype, false);
+}
+
+size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t compute_dtype) {
+  const msign_group_t g = one_group(nullptr, nullptr, batch, rows, cols);
+  return call_workspace(&g, 1, compute_dtype, true);
+}
+
+size_t msign_ns_grouped_workspace_bytes(const msign_group_t* groups, int32_t ngroups, int32_t compute_dtype) {
+  return call_workspace(groups, ngroups, compute_dtype, false);
+}
+
+size_t msign_gram_ns_grouped_workspace_bytes(const msign_group_t* groups, int32_t ngroups,
+                                             int32_t compute_dtype) {
+  return call_workspace(groups, ngroups, compute_dtype, true);
+}
+
+msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
+                        int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
+                        float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const msign_group_t g = one_group(x, y, batch, rows, cols);
+  return ns_run(&g, 1, io_dtype, compute_dtype, steps, coeffs, eps, 0u, workspace, workspace_bytes, stream);
+}
+
+msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
+                           int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
+                           float eps, uint32_t flags, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const msign_group_t g = one_group(x, y, batch, rows, cols);
+  return ns_run(&g, 1, io_dtype, compute_dtype, steps, coeffs, eps, flags, workspace, workspace_bytes, stream);
+}
+
+msign_status_t msign_ns_grouped(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype,
+                                int32_t compute_dtype, int32_t steps, const float* coeffs, float eps,
+                                uint32_t flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return ns_run(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, flags, workspace, workspace_bytes,
+                stream);
+}
+
+msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
+                             int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
+                             float eps, const int32_t* restart_after, int32_t n_restarts, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  const msign_group_t g = one_group(x, y, batch, rows, cols);
+  return gram_run(&g, 1, io_dtype, compute_dtype, steps, coeffs, eps, restart_after, n_restarts, workspace,
+                  workspace_bytes, stream);
+}
+
+size_t muon_step_workspace_bytes(const muon_group_t* groups, int32_t ngroups, int32_t method,
+                                 int32_t compute_dtype) {
+  MuonCall mc;
+  const std::string keep = g_err;
+  const msign_status_t st = plan_muon(groups, ngroups, method, compute_dtype, nullptr, &mc);
+  g_err = keep;
+  return st == MSIGN_OK ? mc.total : (size_t)-1;
+}
+
+msign_status_t muon_step(const muon_group_t* groups, int32_t ngroups, int32_t io_dtype, float mu, float lr,
+                         int32_t method, int32_t compute_dtype, int32_t steps, const float* coeffs, float eps,
+                         uint32_t flags, const int32_t* restart_after, int32_t n_restarts, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return muon_run(groups, ngroups, io_dtype, mu, lr, method, compute_dtype, steps, coeffs, eps, flags,
+                  restart_after, n_restarts, workspace, workspace_bytes, stream);
+}
+
+msign_status_t msign_gram_ns_grouped(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype,
+                                     int32_t compute_dtype, int32_t steps, const float* coeffs, float eps,
+                                     const int32_t* restart_after, int32_t n_restarts, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return gram_run(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, restart_after, n_restarts,
+                  workspace, workspace_bytes, stream);
 }
 
 namespace {

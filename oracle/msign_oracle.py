@@ -18,7 +18,10 @@ passage of the source pages it follows.  Page keys used below:
         Theorem 1), §2.3 (Algorithm 1, naive Gram NS), §2.4 (FLOP count),
         §3.4 (Algorithm 2, stabilised Gram NS with restart), Appendix 1-2.
   [NB]  nil9.net blog index, flash-muon excerpt (the PyTorch loop that forms
-        A = X X^T once and reuses it).
+        A = X X^T once and reuses it; the iterated matrix is the gradient or
+        its momentum).
+  [MS]  anti-entrophic.github.io/posts/10054.html, the Mousse page,
+        §标准 Muon 算法 (the Muon update is -msign of the matrix).
 
 Pins: every function here is checked by the not-gpu tests against closed forms,
 invariants or values the pages print (tests/test_oracle_pins.py).  No function
@@ -274,6 +277,27 @@ def ns_improved_init_single(m: np.ndarray, coeffs=None, steps: int = DEFAULT_STE
 def ns_improved_init(m, coeffs=None, steps: int = DEFAULT_STEPS, eps: float = DEFAULT_EPS):
     """Batched form of `ns_improved_init_single`."""
     return _batched(ns_improved_init_single, m, coeffs=coeffs, steps=steps, eps=eps)
+
+
+# ---------------------------------------------------------------------------
+# Muon step around msign
+# ---------------------------------------------------------------------------
+
+def muon_step(w, g, m, mu: float, lr: float, msign=None):
+    """One Muon update of parameters w with gradient g and momentum m.
+
+    [GR] §1.1 states the update rule with a momentum matrix M_k (M_0 = 0),
+    a momentum coefficient mu and a learning rate eta, but the formula itself
+    is lost in the text; [MS] §标准 Muon 算法 gives the update direction
+    -msign; [NB] applies NS to the gradient or its momentum.  Read as
+        M <- mu M + G,   W <- W - eta msign(M).
+    `msign` is the map applied over the last two dims (default: this
+    module's NS).  Returns (new w, new m), both float64.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    m_new = mu * np.asarray(m, dtype=np.float64) + np.asarray(g, dtype=np.float64)
+    o = (ns if msign is None else msign)(m_new)
+    return w - lr * o, m_new
 
 
 # ---------------------------------------------------------------------------

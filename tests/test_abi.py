@@ -175,3 +175,113 @@ def test_binding_rejects_cpu_tensors():
         mod.msign_ns(torch.zeros(4, 8))
     with pytest.raises(ValueError):
         mod.syrk_xxt(torch.zeros(4, 8))
+
+
+def _garr(*groups):
+    arr = (mod._Group * len(groups))()
+    for i, g in enumerate(groups):
+        arr[i] = mod._Group(*g)
+    return arr
+
+
+def test_grouped_argument_errors():
+    lib = _lib()
+    ok = (0x10000, 0x10000, 1, 8, 16)
+    other = (0x30000, 0x30000, 2, 40, 24)
+
+    def ns(arr, n, ws=FAKE2, wsb=1 << 30):
+        return lib.msign_ns_grouped(arr, n, 1, 1, 5, None, 1e-20, 0, ws, wsb, None)
+
+    assert ns(_garr(ok), 0) == 1
+    assert ns(_garr(ok, ok, ok, ok, ok), 5) == 1
+    assert ns(None, 1) == 1
+    # a bad group is named in the message
+    assert ns(_garr(ok, (0x40000, 0x40000, -1, 8, 16)), 2) == 3
+    assert b"group 1" in lib.msign_last_error()
+    # one group's output over another group's input
+    assert ns(_garr(ok, (0x50000, 0x10000 + 64, 1, 8, 16)), 2) == 5
+    assert b"another" in lib.msign_last_error()
+    # inputs may overlap each other (read only): only the workspace is short
+    assert ns(_garr((0x10000, 0x60000, 1, 8, 16), (0x10000, 0x70000, 1, 8, 16)), 2, wsb=16) == 4
+    assert ns(_garr(ok, other), 2, wsb=16) == 4
+    # all groups empty: a no-op
+    assert ns(_garr((0, 0, 0, 8, 16), (0, 0, 3, 0, 16)), 2, ws=None, wsb=0) == 0
+    g = lib.msign_gram_ns_grouped
+    arr = (ctypes.c_int32 * 1)(5)
+    assert g(_garr(ok, other), 2, 1, 2, 5, None, 1e-20, arr, 1, FAKE2, 1 << 30, None) == 1
+
+
+def test_grouped_workspace_queries():
+    lib = _lib()
+    big = (1 << 64) - 1
+    one = (0, 0, 3, 128, 256)
+    tall = (0, 0, 2, 300, 70)
+    empty = (0, 0, 0, 64, 64)
+    for q, single in ((lib.msign_ns_grouped_workspace_bytes, lib.msign_ns_workspace_bytes),
+                      (lib.msign_gram_ns_grouped_workspace_bytes, lib.msign_gram_ns_workspace_bytes)):
+        # one group is the single-problem call
+        assert q(_garr(one), 1, 1) == single(3, 128, 256, 1)
+        # empty groups are skipped
+        assert q(_garr(one, empty), 2, 1) == q(_garr(one), 1, 1)
+        assert q(_garr(empty), 1, 1) == 0
+        # the groups' own buffers are all there
+        both = q(_garr(one, tall), 2, 1)
+        assert both > max(single(3, 128, 256, 1), single(2, 300, 70, 1))
+        assert q(_garr(one), 0, 1) == big
+        assert q(_garr(one), 1, 9) == big
+        assert q(_garr((0, 0, -1, 8, 8)), 1, 1) == big
+        assert q(None, 1, 1) == big
+
+
+def _marr(*groups):
+    arr = (mod._MuonGroup * len(groups))()
+    for i, g in enumerate(groups):
+        arr[i] = mod._MuonGroup(*g)
+    return arr
+
+
+def test_muon_step_argument_errors():
+    lib = _lib()
+    ok = (0x100000, 0x200000, 0x300000, 1, 8, 16)
+
+    def step(arr, n=1, mu=0.9, lr=0.01, method=0, flags=0, restarts=None, nr=0, ws=FAKE2, wsb=1 << 30, io=1):
+        return lib.muon_step(arr, n, io, mu, lr, method, 1, 5, None, 1e-20, flags, restarts, nr, ws, wsb, None)
+
+    assert step(_marr(ok), n=0) == 1
+    assert step(None) == 1
+    assert step(_marr(ok), method=2) == 1
+    assert step(_marr(ok), mu=float("nan")) == 1
+    assert step(_marr(ok), lr=float("inf")) == 1
+    assert step(_marr(ok), io=7) == 2
+    assert step(_marr(ok), flags=4) == 1
+    assert step(_marr(ok), method=1, flags=1) == 1          # flags are for NS only
+    bad = (ctypes.c_int32 * 1)(9)
+    assert step(_marr(ok), method=1, restarts=bad, nr=1) == 1
+    assert step(_marr((0x100000, 0x200000, None, 1, 8, 16))) == 1
+    assert step(_marr((0x100001, 0x200000, 0x300000, 1, 8, 16))) == 1   # misaligned w
+    assert step(_marr((0x100000, 0x200000, 0x300000, -1, 8, 16))) == 3
+    assert step(_marr(ok), wsb=16) == 4
+    assert step(_marr(ok), ws=ctypes.c_void_p(0x20000010)) == 4
+    # m over w, w over another group's gradient, g inside the workspace
+    assert step(_marr((0x100000, 0x200000, 0x100000 + 64, 1, 8, 16))) == 5
+    assert step(_marr(ok, (0x400000, 0x100000, 0x500000, 1, 8, 16)), n=2) == 5
+    assert step(_marr((0x100000, 0x20000000 + 256, 0x300000, 1, 8, 16))) == 5
+    # gradients may be shared between groups (read only); steps are checked
+    # before anything is launched
+    assert lib.muon_step(_marr(ok), 1, 1, 0.9, 0.01, 0, 1, 0, None, 1e-20, 0, None, 0, FAKE2, 1 << 30,
+                         None) == 1
+    # every group empty: a no-op
+    assert step(_marr((0, 0, 0, 0, 8, 16)), ws=None, wsb=0) == 0
+
+
+def test_muon_step_workspace_query():
+    lib = _lib()
+    big = (1 << 64) - 1
+    for b, r, c in ((3, 128, 256), (2, 300, 70)):
+        arr = _marr((0, 0, 0, b, r, c))
+        o_bytes = (b * r * c * 4 + 255) // 256 * 256
+        assert lib.muon_step_workspace_bytes(arr, 1, 0, 1) == o_bytes + lib.msign_ns_workspace_bytes(b, r, c, 1)
+        assert lib.muon_step_workspace_bytes(arr, 1, 1, 2) == o_bytes + lib.msign_gram_ns_workspace_bytes(b, r, c, 2)
+    assert lib.muon_step_workspace_bytes(_marr((0, 0, 0, 0, 8, 8)), 1, 0, 1) == 0
+    assert lib.muon_step_workspace_bytes(_marr((0, 0, 0, 1, 8, 8)), 1, 5, 1) == big
+    assert lib.muon_step_workspace_bytes(_marr((0, 0, 0, 1, 8, 8)), 0, 0, 1) == big

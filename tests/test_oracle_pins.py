@@ -327,3 +327,58 @@ def test_flop_models_reproduce_printed_reductions():
     assert O.naive_gram_flops(n, 2 * n) == (17 + 3 * 2) * n ** 3
     assert O.symmetric_ns_flops(n, 4 * n, 1) == (3 * 4 + 1) * n ** 3
     assert O.restart_gram_flops(n, 8 * n) == (14 + 6 * 8) * n ** 3
+
+
+# --- Muon step around msign --------------------------------------------------------
+
+def _orthogonal(n, seed):
+    q, r = np.linalg.qr(_rand((n, n), seed))
+    return q * np.sign(np.diag(r))
+
+
+def test_muon_two_steps_closed_form():
+    """With exact msign and M_0 = 0: G_1 = Q_1 (orthogonal) and
+    G_2 = P Q_2 - mu Q_1 (P symmetric positive definite) give M_1 = Q_1,
+    M_2 = P Q_2, whose polar factor is Q_2, so W_2 = W_0 - eta (Q_1 + Q_2).
+    Any other momentum rule (M + mu G, mu (M + G), (1 - mu) M + G ...) or a
+    sign slip in the update moves W_2 off this value."""
+    n, mu, lr = 24, 0.9, 0.05
+    q1, q2 = _orthogonal(n, 501), _orthogonal(n, 502)
+    b = _rand((n, n), 503)
+    p = b @ b.T + n * np.eye(n)
+    w0 = _rand((n, n), 504)
+    w1, m1 = O.muon_step(w0, q1, np.zeros((n, n)), mu, lr, msign=O.exact_msign)
+    assert np.allclose(m1, q1, atol=1e-14)
+    w2, m2 = O.muon_step(w1, p @ q2 - mu * q1, m1, mu, lr, msign=O.exact_msign)
+    assert np.allclose(m2, p @ q2, atol=1e-12)
+    assert np.allclose(w2, w0 - lr * (q1 + q2), atol=1e-12)
+
+
+def test_muon_constant_gradient_and_rectangular_shapes():
+    """A constant gradient G makes M_k = (1 + mu + ... + mu^(k-1)) G, a positive
+    multiple of G, so every step moves W by -eta msign(G) (scale invariance of
+    msign); holds for wide and tall batches with the NS map as well."""
+    mu, lr = 0.95, 0.02
+    for shape in ((2, 16, 40), (2, 40, 16)):
+        g = _rand(shape, 510 + shape[1])
+        w = _rand(shape, 520 + shape[1])
+        m = np.zeros(shape)
+        d_exact = O.exact_msign(g)
+        d_ns = O.ns(g)
+        for k in range(1, 4):
+            w_next, m = O.muon_step(w, g, m, mu, lr)
+            assert np.allclose(m, sum(mu ** j for j in range(k)) * g, atol=1e-12)
+            assert np.allclose(w - w_next, lr * d_ns, atol=1e-10)
+            w = w_next
+        # the NS direction is the exact one up to NS's own error bound
+        assert O.max_rel_fro_error(d_ns, d_exact) < 0.35
+
+
+def test_muon_zero_momentum_coefficient_is_plain_msign_descent():
+    """mu = 0: the momentum is the gradient, and the step is [MS]'s
+    -eta msign(G) with eta = 1."""
+    g = _rand((3, 12, 20), 530)
+    w = _rand((3, 12, 20), 531)
+    w1, m1 = O.muon_step(w, g, _rand((3, 12, 20), 532), 0.0, 1.0, msign=O.exact_msign)
+    assert np.array_equal(m1, g)
+    assert np.allclose(w1, w - O.exact_msign(g), atol=1e-13)
