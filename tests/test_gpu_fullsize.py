@@ -1,5 +1,6 @@
 """Parity at the workloads' full sizes, in the launch configuration the
-benchmark times (each shape group as one batched call).  The fp64 oracle
+benchmark times (a single batched call, or one grouped call over the shape
+groups of a workload).  The fp64 oracle
 runs on sampled matrices of each batch (first and last), one at a time.
 BLAS threads are capped at 16 (one GPU's share of the host)."""
 
@@ -73,27 +74,61 @@ def test_square_8192_syrk_unit():
     assert np.all(np.abs(got - ref) <= scale * (2.0 ** -8 + 2 * 8192 * 2.0 ** -24))
 
 
+def _run_grouped(M, workload, method, cdt):
+    xs = [S.group_batch(gr, device="cuda") for gr in S.WORKLOADS[workload].groups]
+    if method == "ns":
+        ys = M.msign_ns_grouped(xs, compute_dtype=cdt)
+    else:
+        ys = M.msign_gram_ns_grouped(xs, compute_dtype=cdt, restart_after=(2,))
+    torch.cuda.synchronize()
+    return xs, ys
+
+
 @pytest.mark.timeout(900)
 def test_transformer_block_ns_bf16():
     M = require_gpu()
-    for gi, gr in enumerate(S.WORKLOADS["c4_block_bf16"].groups):
-        announce(f"msign_ns block group {gi}: {gr.batch}x{gr.rows}x{gr.cols}")
-        x, y = _run_group(M, gr, "ns", torch.bfloat16)
+    announce("msign_ns_grouped block: 16x4096x4096 + 16x14336x4096")
+    xs, ys = _run_grouped(M, "c4_block_bf16", "ns", torch.bfloat16)
+    for gi, (x, y) in enumerate(zip(xs, ys)):
         _check_samples(x, y, 2e-2, f"block group {gi}")
-        del x, y
-        torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("method,cdt", [("gram", torch.float16), ("ns", torch.bfloat16)])
 def test_moe_experts(method, cdt):
     M = require_gpu()
-    for gi, gr in enumerate(S.WORKLOADS["c5_moe_f16"].groups):
-        announce(f"{method} moe group {gi}: {gr.batch}x{gr.rows}x{gr.cols}")
-        x, y = _run_group(M, gr, method, cdt)
+    announce(f"{method} grouped moe: 64x2048x7168 + 8x1024x8192")
+    xs, ys = _run_grouped(M, "c5_moe_f16", method, cdt)
+    for gi, (x, y) in enumerate(zip(xs, ys)):
         _check_samples(x, y, 2e-2, f"moe {method} group {gi}")
-        del x, y
-        torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_transformer_block_muon_step():
+    """One Muon step over the block's two shape groups (the workload as
+    gradients, bf16 parameters, fp32 momentum holding a previous step's
+    value), checked on sampled matrices against the oracle's muon_step."""
+    M = require_gpu()
+    announce("muon_step block: 16x4096x4096 + 16x14336x4096")
+    gs = [S.group_batch(gr, device="cuda") for gr in S.WORKLOADS["c4_block_bf16"].groups]
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    ws = [(0.02 * torch.randn(g.shape, generator=gen, device="cuda")).to(torch.bfloat16) for g in gs]
+    ms = [0.5 * g.float() for g in gs]
+    w0 = [w.clone() for w in ws]
+    m0 = [m.clone() for m in ms]
+    mu, lr = 0.95, 0.02
+    M.muon_step(ws, gs, ms, lr=lr, mu=mu, method="ns", compute_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for gi in range(len(gs)):
+        for i in sorted({0, gs[gi].shape[0] - 1}):
+            announce(f"muon block group {gi}: oracle on matrix {i}")
+            w_ref, m_ref = O.muon_step(f64(w0[gi][i]), f64(gs[gi][i]), f64(m0[gi][i]), mu, lr,
+                                       msign=O.ns_single)
+            assert np.linalg.norm(f64(ms[gi][i]) - m_ref) <= 1e-6 * np.linalg.norm(m_ref)
+            d_ref = f64(w0[gi][i]) - w_ref
+            d_gpu = f64(w0[gi][i]) - f64(ws[gi][i])
+            bound = 2e-2 * np.linalg.norm(d_ref) + 2.0 ** -9 * np.linalg.norm(w_ref)
+            assert np.linalg.norm(d_gpu - d_ref) <= bound, (gi, i)
 
 
 @pytest.mark.timeout(900)
