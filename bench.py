@@ -57,6 +57,31 @@ def dense_flops(n, m, steps=5):
     return steps * (4.0 * m * n * n + 2.0 * n ** 3)
 
 
+def algorithmic_flops(n, m, method, steps=5):
+    """Flops the method executes per msign ("Gram Newton-Schulz" §2.4 and
+    §3.4 counts): symmetric NS T (3 alpha + 1) n^3; Gram NS with one restart
+    (14 + 6 alpha) n^3 at T = 5."""
+    if method == "gram":
+        return (14.0 * n + 6.0 * m) * n * n
+    return steps * (3.0 * m + n) * n * n
+
+
+def mfma_loop_peak(M, dtype, launches=5, iters=20000):
+    """TFLOP/s of the MFMA-only probe kernel (operands in registers, every
+    SIMD busy): the matrix rate the chip sustains, clock limits included."""
+    import torch
+    from msign_newton_schulz_amd import _binding as B
+    out = torch.empty(B.PROBE_BLOCKS * B.PROBE_THREADS, dtype=torch.float32, device="cuda")
+    M.mfma_probe(2000, dtype, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = sum(M.mfma_probe(iters, dtype, out=out) for _ in range(launches))
+    e1.record()
+    torch.cuda.synchronize()
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def class_flops(n, m):
     """Algorithmic flops of one launch of each kernel class on one matrix
     ("Gram Newton-Schulz" §2.4 counts): a triangle product counts half of the
@@ -263,12 +288,14 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
     elapsed = t1 - t0
     nmat = sum(x.shape[0] for x in xs)
     eff = 0.0
+    alg = 0.0
     cls_flops = {"xxt": 0.0, "square": 0.0, "rect": 0.0}
     shapes = []
     for x in xs:
         b, r, c = x.shape
         n_, m_ = min(r, c), max(r, c)
         eff += b * dense_flops(n_, m_)
+        alg += b * algorithmic_flops(n_, m_, method)
         shapes.append([int(b), int(r), int(c)])
         for k, v in class_flops(n_, m_).items():
             cls_flops[k] += b * v
@@ -287,6 +314,7 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
                    "parallelism": "single GPU"},
         "effective_tflops": eff_tflops,
         "effective_frac_of_peak": eff_tflops / PEAK_TFLOPS[cdt],
+        "algorithmic_tflops": alg * steps / elapsed / 1e12,
     }
     if plain_ms is not None:
         rec["ms_per_step_without_events"] = plain_ms
@@ -309,6 +337,13 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
                                "traffic": recorded_traffic(workload, dom),
                                "avg_launch_us": avg_s * 1e6,
                                "algorithmic_flops_per_launch": flops_per_launch}
+            if cdt in ("bf16", "f16"):
+                # beside the published peak: the MFMA-only loop on this GPU
+                loop = mfma_loop_peak(M, tdt)
+                rec["mfma_loop_peak"] = {"value": loop, "unit": "TFLOP/s", "dtype": cdt,
+                                         "kernel": "mfma_probe_kernel (16x16x32, operands in registers)"}
+                rec["roofline"]["frac_of_loop_peak"] = ach / loop
+                rec["effective_frac_of_loop_peak"] = eff_tflops / loop
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(wl, method)
     return rec
@@ -320,8 +355,8 @@ def main():
         copy_calibration(args.copy_bytes)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(msign shards by batch across GPUs with no exchange; see the design notes)",
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(msign shards by batch across GPUs, each GPU running its share with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     if args.all:

@@ -314,6 +314,23 @@ const char* msign_version(void);
 msign_status_t msign_kernel_timing_enable(int32_t enable);
 msign_status_t msign_kernel_timing_read(double* total_ms, int64_t* launches);
 
+/*
+ * msign_mfma_probe - measurement only: one launch of a kernel that issues
+ * nothing but 16x16x32 MFMAs (bf16 or fp16 operands, fp32 accumulation)
+ * from registers, MSIGN_PROBE_BLOCKS blocks of MSIGN_PROBE_THREADS threads
+ * (8 waves per CU, 2 per SIMD, 8 independent accumulator chains per wave),
+ * `iters` rounds of 8 MFMAs per wave.  Timing it gives the matrix rate the
+ * chip sustains (its clock under load), the denominator beside the
+ * published peak.  Flops per launch: MSIGN_PROBE_FLOPS_PER_ITER * iters.
+ *   dtype  MSIGN_BF16 or MSIGN_F16.
+ *   out    device, MSIGN_PROBE_BLOCKS * MSIGN_PROBE_THREADS floats (one
+ *          per thread; keeps the result alive, values meaningless).
+ */
+#define MSIGN_PROBE_BLOCKS 512
+#define MSIGN_PROBE_THREADS 256
+#define MSIGN_PROBE_FLOPS_PER_ITER (512.0 * 4 * 8 * 16 * 16 * 32 * 2)
+msign_status_t msign_mfma_probe(int32_t dtype, int32_t iters, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,10 +6,10 @@ built (`python -m msign_newton_schulz_amd.build`) before use.
 """
 
 from ._binding import (F32, BF16, F16, LIB_PATH, MAX_GROUPS, MsignError,  # noqa: F401
-                       gram_ns_workspace_bytes, kernel_timing, library, msign_gram_ns,
+                       gram_ns_workspace_bytes, kernel_timing, library, mfma_probe, msign_gram_ns,
                        msign_gram_ns_grouped, msign_ns, msign_ns_grouped, muon_step, ns_workspace_bytes,
                        read_kernel_timing, syrk_xxt, version)
 
 __all__ = ["msign_ns", "msign_gram_ns", "msign_ns_grouped", "msign_gram_ns_grouped", "muon_step", "syrk_xxt", "MsignError", "library", "version",
            "ns_workspace_bytes", "gram_ns_workspace_bytes", "kernel_timing", "read_kernel_timing",
-           "LIB_PATH", "MAX_GROUPS", "F32", "BF16", "F16"]
+           "mfma_probe", "LIB_PATH", "MAX_GROUPS", "F32", "BF16", "F16"]

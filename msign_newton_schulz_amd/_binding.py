@@ -90,6 +90,8 @@ def _load():
     lib.muon_step_workspace_bytes.restype = sz
     lib.muon_step.argtypes = [mp, i32, i32, f, f, i32, i32, i32, fp, f, ctypes.c_uint32, ip, i32, vp, sz, vp]
     lib.muon_step.restype = ctypes.c_int
+    lib.msign_mfma_probe.argtypes = [i32, i32, vp, vp]
+    lib.msign_mfma_probe.restype = ctypes.c_int
     lib.msign_status_string.argtypes = [ctypes.c_int]
     lib.msign_status_string.restype = ctypes.c_char_p
     lib.msign_last_error.argtypes = []
@@ -343,6 +345,23 @@ def muon_step(params: Sequence[torch.Tensor], grads: Sequence[torch.Tensor],
         st = lib.muon_step(arr, len(params), io, float(mu), float(lr), meth, cdt, steps, carr, float(eps),
                            flags, rarr, len(rs), ws.data_ptr(), ws.numel(), _stream_handle(params[0].device))
     _check(st)
+
+
+PROBE_BLOCKS, PROBE_THREADS = 512, 256
+PROBE_FLOPS_PER_ITER = 512.0 * 4 * 8 * 16 * 16 * 32 * 2  # MSIGN_PROBE_FLOPS_PER_ITER
+
+
+def mfma_probe(iters: int, dtype=torch.bfloat16, device="cuda", out: Optional[torch.Tensor] = None) -> float:
+    """Queue one MFMA-only launch (C ABI `msign_mfma_probe`, measurement
+    only) on the current stream; returns its flop count."""
+    lib = _load()
+    if out is None:
+        out = torch.empty(PROBE_BLOCKS * PROBE_THREADS, dtype=torch.float32, device=device)
+    _check_cuda(out)
+    with torch.cuda.device(out.device):
+        st = lib.msign_mfma_probe(_dt(dtype), int(iters), out.data_ptr(), _stream_handle(out.device))
+    _check(st)
+    return PROBE_FLOPS_PER_ITER * iters
 
 
 def syrk_xxt(x: torch.Tensor, alpha: float = 1.0, d: Optional[torch.Tensor] = None,

@@ -26,6 +26,7 @@
 #include "gemm_nt.hpp"
 #include "init_scale.hpp"
 #include "launch.hpp"
+#include "mfma_probe.hpp"
 #include "muon.hpp"
 #include "normalize.hpp"
 
@@ -1205,6 +1206,20 @@ const char* msign_status_string(msign_status_t status) {
 }
 
 const char* msign_last_error(void) { return g_err.c_str(); }
+
+msign_status_t msign_mfma_probe(int32_t dtype, int32_t iters, float* out, hipStream_t stream) {
+  g_err.clear();
+  static_assert(kProbeBlocks == MSIGN_PROBE_BLOCKS && kProbeThreads == MSIGN_PROBE_THREADS, "probe layout");
+  if (dtype != MSIGN_BF16 && dtype != MSIGN_F16) return fail(MSIGN_ERR_DTYPE, "dtype must be MSIGN_BF16 or MSIGN_F16");
+  if (iters < 1) return fail(MSIGN_ERR_ARG, "iters must be >= 1");
+  if (!out || !aligned(out, 4)) return fail(MSIGN_ERR_ARG, "out must be a non-null float buffer");
+  if (dtype == MSIGN_BF16)
+    mfma_probe_kernel<bf16_t><<<kProbeBlocks, kProbeThreads, 0, stream>>>(iters, 0.5f, out);
+  else
+    mfma_probe_kernel<f16_t><<<kProbeBlocks, kProbeThreads, 0, stream>>>(iters, 0.5f, out);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MSIGN_OK : hip_fail(e, "mfma_probe_kernel");
+}
 
 const char* msign_version(void) { return "msign 0.1.0 gfx950"; }
 

@@ -285,3 +285,11 @@ def test_muon_step_workspace_query():
     assert lib.muon_step_workspace_bytes(_marr((0, 0, 0, 0, 8, 8)), 1, 0, 1) == 0
     assert lib.muon_step_workspace_bytes(_marr((0, 0, 0, 1, 8, 8)), 1, 5, 1) == big
     assert lib.muon_step_workspace_bytes(_marr((0, 0, 0, 1, 8, 8)), 0, 0, 1) == big
+
+
+def test_mfma_probe_argument_errors():
+    lib = _lib()
+    assert lib.msign_mfma_probe(0, 10, FAKE2, None) == 2      # fp32 has no 16x16x32 form
+    assert lib.msign_mfma_probe(1, 0, FAKE2, None) == 1
+    assert lib.msign_mfma_probe(1, 10, None, None) == 1
+    assert lib.msign_mfma_probe(1, 10, ctypes.c_void_p(0x20000001), None) == 1
