@@ -129,3 +129,32 @@ def test_grouped_rejects_mixed_dtypes():
         M.msign_ns_grouped([a, b])
     with pytest.raises(ValueError):
         M.msign_ns_grouped([a] * 5)
+
+
+@pytest.mark.parametrize("trial", range(6))
+def test_grouped_random_shapes(trial):
+    """Seeded random groupings: 2-4 groups, batches 1-3, ragged sizes from
+    1 to 700 on either side (wide, tall, vectors), NS and Gram alternately.
+    Gram trials draw aspect ratios >= 2 (the method's regime; it squares
+    the condition number)."""
+    M = require_gpu()
+    rng = np.random.default_rng(9000 + trial)
+    ng = int(rng.integers(2, 5))
+    gram = trial % 2 == 1
+    shapes = []
+    for _ in range(ng):
+        b = int(rng.integers(1, 4))
+        if gram:
+            n = int(rng.integers(1, 300))
+            m = 2 * n + int(rng.integers(0, 300))
+            shapes.append((b, n, m) if rng.integers(0, 2) else (b, m, n))
+        else:
+            shapes.append((b, int(rng.integers(1, 701)), int(rng.integers(1, 701))))
+    announce(f"grouped random trial {trial}: {'gram' if gram else 'ns'} {shapes}")
+    xs = _inputs(shapes, "f32", 9100 + 10 * trial)
+    if gram:
+        ys = M.msign_gram_ns_grouped([x.cuda() for x in xs], compute_dtype=torch.float32)
+    else:
+        ys = M.msign_ns_grouped([x.cuda() for x in xs], compute_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_groups(ys, xs, O.ns, 1e-4)
