@@ -170,8 +170,11 @@ msign_status_t msign_gram_ns(const void* x, void* y, int64_t batch,
  * all groups (longest contraction first), so a small group fills the CUs
  * that a large group's last round of tiles leaves idle, and the launch
  * count does not grow with the number of groups.  Each matrix gets the
- * result that a call on its group alone would give, up to the last bits
- * (the K split of the last round of tiles depends on the whole launch).
+ * result of a call on its group alone up to rounding: a launch's tile size
+ * and K split depend on all of its groups, which changes the order of the
+ * fp32 sums, and the iteration carries such last-bit differences through
+ * its rounded operands (both results stay within the same error of the
+ * exact iteration).  A grouped call is itself bit-stable.
  *
  * Group g: x, y device [batch, rows, cols] in io_dtype, as in msign_ns (y ==
  * x allowed).  Groups with batch, rows or cols equal to 0 are skipped.  An
