@@ -91,6 +91,23 @@ def test_graph_replays_match_eager():
         assert torch.equal(ya, refa) and torch.equal(yb, refb), k
 
 
+def test_graph_replays_of_gram_ns_match_eager():
+    M = require_gpu()
+    announce("msign_gram_ns captured in a graph")
+    x = _x(256, 1024, 31, dt="f16")
+    y = torch.empty_like(x)
+    ws = torch.empty(M.gram_ns_workspace_bytes(2, 256, 1024, torch.float16), dtype=torch.uint8, device="cuda")
+    g = _capture(lambda: M.msign_gram_ns(x, compute_dtype=torch.float16, out=y, workspace=ws))
+    for k in range(4):
+        x.copy_(_x(256, 1024, 400 + k, dt="f16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = M.msign_gram_ns(x, compute_dtype=torch.float16)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), k
+
+
 def test_graph_replays_of_a_muon_step_match_eager_steps():
     M = require_gpu()
     announce("muon_step captured in a graph, replayed 3 times")
