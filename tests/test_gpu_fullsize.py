@@ -56,6 +56,22 @@ def test_square_8192_ns_bf16():
     _check_samples(x, y, 2e-2, "8192^2 ns")
 
 
+@pytest.mark.timeout(900)
+def test_square_8192_ns_improved_init_bf16():
+    """The benchmark's improved-initial-normalisation case at full size,
+    against the oracle's version of it."""
+    M = require_gpu()
+    gr = S.WORKLOADS["c3_8192x8192_bf16"].groups[0]
+    announce("msign_ns improved init 8192x8192 bf16")
+    x = S.group_batch(gr, device="cuda")
+    y = M.msign_ns(x, compute_dtype=torch.bfloat16, improved_init=True)
+    torch.cuda.synchronize()
+    announce("8192^2 improved init: oracle on matrix 0")
+    ref = O.ns_improved_init_single(f64(x[0]))
+    err = O.max_rel_fro_error(f64(y[0])[None], ref[None])
+    assert err <= 2e-2, err
+
+
 @pytest.mark.timeout(600)
 def test_square_8192_syrk_unit():
     M = require_gpu()
