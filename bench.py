@@ -90,6 +90,26 @@ def class_flops(n, m):
     return {"xxt": float(m) * n * n, "square": float(n) ** 3, "rect": 2.0 * m * n * n}
 
 
+def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
+    """Algorithmic HBM bytes of the class-0 (HBM-bound) passes of one msign on
+    one matrix: the sum of squares reads the input; the normalise pass reads
+    it again and writes the fp32 master (NS only) and the compute-dtype copy,
+    padded to 64 (rows and columns).  The improved initial normalisation adds
+    its combine pass (reads A and A A, writes B); a Muon step adds the
+    momentum pass (reads M fp32 and G, writes M) and the update (reads W and
+    the fp32 direction, writes W), and its msign input is the fp32 M."""
+    pad = lambda v: (v + 63) // 64 * 64
+    n, m = min(rows, cols), max(rows, cols)
+    elems, padded = rows * cols, pad(n) * pad(m)
+    x_bytes = 4 if method == "muon_ns" else io_bytes
+    b = 2 * elems * x_bytes + padded * (c_bytes + (0 if method == "gram" else 4))
+    if method == "ns_init":
+        b += 3 * pad(n) * pad(n) * c_bytes
+    if method == "muon_ns":
+        b += elems * (4 + io_bytes + 4) + elems * (io_bytes + 4 + io_bytes)
+    return float(b)
+
+
 # Counter summary of the dominant kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE
 # passes, scaled by the same counters on a plain copy of known size).  Its
 # traffic figure is reported only while the kernel sources hash to the value
@@ -324,6 +344,19 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
             tot, cnt = probe[k]
             per[k] = {"total_ms": tot, "launches": cnt, "avg_us": 1e3 * tot / cnt if cnt else None}
         rec["kernels_one_step"] = per
+        # the HBM-bound passes (normalise and the like): algorithmic bytes of
+        # one step over their event-timed duration in the probe step
+        tot, cnt = probe["normalize"]
+        if cnt and tot > 0:
+            nbytes = 0.0
+            for x in xs:
+                b, r, c = x.shape
+                nbytes += b * elementwise_bytes(r, c, method, x.element_size(),
+                                                {"bf16": 2, "f16": 2, "f32": 4}[cdt])
+            rec["normalize_hbm"] = {"bound": "hbm", "achieved": nbytes / (tot * 1e-3) / 1e9,
+                                    "peak": HBM_GBS, "unit": "GB/s",
+                                    "frac": nbytes / (tot * 1e-3) / 1e9 / HBM_GBS,
+                                    "bytes_per_step": nbytes, "launches": cnt}
         tot, cnt = ktime[dom]
         if cnt:
             # one launch of a class processes every group's whole batch (a
