@@ -508,9 +508,21 @@ msign_status_t launch_normalize(const void* x, int32_t io_dtype, int64_t batch, 
     p.out[k] = outs_x[k];
     p.out[k].transposed = s.tall ? !outs_x[k].transposed : outs_x[k].transposed;
   }
+  // no transposed output and whole 16-byte chunks per input row: the
+  // direct kernel (no LDS tile), else the tiled one
+  bool direct = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && cols % (io_dtype == MSIGN_F32 ? 4 : 8) == 0 &&
+                p.cols_pad % 8 == 0;
+  for (int k = 0; k < nout; ++k)
+    direct = direct && !p.out[k].transposed && p.out[k].ld % 8 == 0 && p.out[k].bstride % 8 == 0 &&
+             aligned(p.out[k].ptr, 16);
   TimedLaunch tl(KC_NORM, st);
-  dim3 g2((unsigned)((p.cols_pad + 63) / 64), (unsigned)((p.rows_pad + 63) / 64), (unsigned)batch);
-  normalize_kernel<<<g2, 256, 0, st>>>(p);
+  if (direct) {
+    dim3 g3((unsigned)((p.cols_pad + 255) / 256), (unsigned)((p.rows_pad + 63) / 64), (unsigned)batch);
+    normalize_direct_kernel<<<g3, 256, 0, st>>>(p);
+  } else {
+    dim3 g2((unsigned)((p.cols_pad + 63) / 64), (unsigned)((p.rows_pad + 63) / 64), (unsigned)batch);
+    normalize_kernel<<<g2, 256, 0, st>>>(p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "normalize_kernel");
   return MSIGN_OK;

@@ -180,4 +180,65 @@ normalize_kernel(const NormParams p) {
   }
 }
 
+// normalize_direct_kernel: the same normalisation when no output is
+// transposed and the input rows hold whole 16-byte chunks (every wide
+// input).  No LDS tile: each thread scales 8 consecutive elements of a row
+// straight from its load into its stores; a block covers 64 rows x 256
+// columns of the padded extent (zeros past the input).  The scale comes from
+// the matrix's partial sums, added by all 256 threads in a fixed order.
+__global__ void __launch_bounds__(256)
+normalize_direct_kernel(const NormParams p) {
+  __shared__ float wsum[4];
+  const int64_t b = blockIdx.z;
+  const int tid = threadIdx.x;
+  float sc = 1.f;
+  if (p.partial != nullptr) {
+    float s = 0.f;
+    for (int i = tid; i < p.nblk; i += 256) s += p.partial[b * p.nblk + i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = s;
+    __syncthreads();
+    sc = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) + p.eps);
+  }
+  const int64_t xb = b * p.rows * p.cols;
+  const int c = blockIdx.x * 256 + (tid & 31) * 8;  // first of this thread's 8 columns
+  if (c >= p.cols_pad) return;
+  for (int rr = tid >> 5; rr < 64; rr += 8) {
+    const int64_t r = (int64_t)blockIdx.y * 64 + rr;
+    if (r >= p.rows_pad) break;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    if (r < p.rows) {
+      const int64_t e = xb + r * p.cols + c;
+      if (p.x_dtype != DT_F32) {
+        if (c < p.cols) {  // cols is a multiple of 8: the chunk is whole
+          const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint16_t lo = u[k] & 0xffff, hi = u[k] >> 16;
+            v[2 * k] = (p.x_dtype == DT_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo)) * sc;
+            v[2 * k + 1] = (p.x_dtype == DT_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi)) * sc;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (c + 4 * h < p.cols) {  // cols is a multiple of 4
+            const f32x4 u = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.x) + e + 4 * h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[4 * h + k] = u[k] * sc;
+          }
+      }
+    }
+    for (int o = 0; o < p.nout; ++o) {
+      const NormOut& os = p.out[o];
+      const int64_t base = b * os.bstride + r * os.ld + c;
+      store_vec4(os.ptr, base, os.dtype, v);
+      store_vec4(os.ptr, base + 4, os.dtype, v + 4);
+    }
+  }
+}
+
 }  // namespace msign
