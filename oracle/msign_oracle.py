@@ -161,12 +161,17 @@ def ns_single(m: np.ndarray, coeffs=None, steps: int = DEFAULT_STEPS,
     """
     m = np.asarray(m, dtype=np.float64)
     x, tall = _as_wide(m)
-    x = frobenius_normalize(x, eps)
-    for a, b, c in coefficient_schedule(coeffs, steps):
+    x = _quintic_steps(frobenius_normalize(x, eps), coefficient_schedule(coeffs, steps))
+    return x.T if tall else x
+
+
+def _quintic_steps(x: np.ndarray, sched) -> np.ndarray:
+    """The NS steps X <- a X + (b A + c A A) X, A = X X^T, from a given X_0."""
+    for a, b, c in sched:
         A = x @ x.T
         B = b * A + c * (A @ A)
         x = a * x + B @ x
-    return x.T if tall else x
+    return x
 
 
 def gram_ns_single(m: np.ndarray, coeffs=None, steps: int = DEFAULT_STEPS,
@@ -256,21 +261,24 @@ def ns_improved_init_single(m: np.ndarray, coeffs=None, steps: int = DEFAULT_STE
                             eps: float = DEFAULT_EPS) -> np.ndarray:
     """NS with the improved initial normalisation of [KX] §改良初值.
 
-    After the Frobenius normalisation, the first step forms A = X X^T and
-    A2 = A A as usual, then divides by s = (sum(A2^2) + eps)^(1/8), i.e. the
-    fourth root of ||(X X^T)^2||_F: X <- X/s, A <- A/s^2, A2 <- A2/s^4, before
-    the first update.  Later steps are unchanged.
+    The section bounds the largest singular value by the chain
+    sigma_1 <= (sum sigma_i^8)^(1/8) <= (sum sigma_i^4)^(1/4) <= ||M||_F and
+    proposes dividing by the eighth-root term, the fourth root of
+    ||(M M^T)^2||_F, instead of by ||M||_F.  It notes that this factor is free
+    inside the iteration because X_0 X_0^T and its square are formed anyway,
+    so it is taken from the Frobenius-normalised X_0.  Written here from that
+    definition: with lambda_i the eigenvalues of X_0 X_0^T (= sigma_i(X_0)^2),
+        s = (sum_i lambda_i^4 + eps)^(1/8),
+    then the plain NS steps run from X_0 / s.  eps sits where the Frobenius
+    normalisation puts it (under the root; 1e-20 by default), which only
+    matters for an all-zero input.
     """
     m = np.asarray(m, dtype=np.float64)
     x, tall = _as_wide(m)
-    x = frobenius_normalize(x, eps)
-    for t, (a, b, c) in enumerate(coefficient_schedule(coeffs, steps)):
-        A = x @ x.T
-        A2 = A @ A
-        if t == 0:
-            s = (float(np.sum(A2 * A2)) + eps) ** 0.125
-            x, A, A2 = x / s, A / s ** 2, A2 / s ** 4
-        x = a * x + (b * A + c * A2) @ x
+    x0 = frobenius_normalize(x, eps)
+    lam = np.linalg.eigvalsh(x0 @ x0.T)
+    s = (float(np.sum(lam ** 4)) + eps) ** 0.125
+    x = _quintic_steps(x0 / s, coefficient_schedule(coeffs, steps))
     return x.T if tall else x
 
 
