@@ -3,8 +3,11 @@
 Default: the square 8192 x 8192 bf16 workload (iid N(0,1)), 5-step quintic NS
 with bf16 products, one msign per step.  Prints ONE JSON line with
 matrices/s, effective TFLOP/s ((20 alpha + 10) n^3 per msign) as a fraction
-of the bf16 dense MFMA peak, the roofline of the dominant kernel (timed with
-HIP events on the launch stream inside the timed region) and the fp64 CPU
+of the bf16 dense MFMA peak (timed without events), the roofline of the
+dominant kernel (a second pass of the same steps with HIP events on the launch
+stream around that kernel's launches), comparisons the pages quote (the
+symmetric X X^T against full-tile and library products, NS with full-tile
+products, Gram against standard NS at alpha = 4 and 8) and the fp64 CPU
 oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--case NAME]
@@ -116,7 +119,7 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
 # recorded with it; after any change to them it is stale and `traffic` is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_rect_8192x8192_bf16_traffic.md")
 KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "init_scale.hpp", "launch.hpp", "launch_impl.hpp", "muon.hpp",
-                  "msign_api.hip", "products_grouped.hip", "products_single.hip")
+                  "msign_api.hip", "products_dense.hip", "products_grouped.hip", "products_single.hip")
 
 
 def kernel_source_hash():
@@ -159,6 +162,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--all", default=None, help="run every case, one JSON line each, into this file")
     ap.add_argument("--no-timing", action="store_true", help="no per-kernel event timing")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparisons the default case carries (unit bench, dense NS, Gram vs NS)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of msign, run 3 plain device copies of this many bytes "
                          "(calibrates the HBM traffic counters)")
@@ -226,7 +231,8 @@ def cpu_baseline(wl, method, sample_seconds=30.0):
                          + ("" if steps_run == 5 else ", scaled x5/2"))
         total = sum(b * t for b, t in per_matrix)
         nmat = sum(b for b, _ in per_matrix)
-        return {"value": nmat / total, "unit": "matrices/s", "cores": cores, "kind": "oracle",
+        return {"value": nmat / total, "unit": "matrices/s", "cores": cores,
+                "host_cpu_count": os.cpu_count(), "kind": "oracle",
                 "sample": "fp64 NumPy oracle (" + method + "), " + "; ".join(descr)
                           + f"; batch mix {[b for b, _ in per_matrix]} weighted"}
     finally:
@@ -234,7 +240,7 @@ def cpu_baseline(wl, method, sample_seconds=30.0):
             ctx.__exit__(None, None, None)
 
 
-def run_case(name, steps, warmup, with_cpu, with_timing):
+def run_case(name, steps, warmup, with_cpu, with_timing, with_extras=False):
     import torch
     import msign_newton_schulz_amd as M
 
@@ -274,36 +280,34 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
     for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
-    probe = dom = None
-    if with_timing:
-        # one more untimed step with every class timed: the per-class
-        # breakdown and the dominant product class
-        M.kernel_timing(True)
-        one_step()
-        torch.cuda.synchronize()
-        probe = M.read_kernel_timing()
-        M.kernel_timing(False)
-        # the timed region brackets only the dominant class's launches
-        dom = max(("xxt", "square", "rect"), key=lambda k: probe[k][0])
-        M.kernel_timing(True, classes=[dom])
-    torch.cuda.synchronize()
+    # the timed region: K whole steps, no events
     t0 = time.perf_counter()
     for _ in range(steps):
         one_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ktime = M.read_kernel_timing() if with_timing else None
-    plain_ms = None
+    probe = dom = ktime = None
+    events_ms = None
     if with_timing:
+        # one more step with every class timed: the per-class breakdown and
+        # the dominant product class
+        M.kernel_timing(True)
+        one_step()
+        torch.cuda.synchronize()
+        probe = M.read_kernel_timing()
         M.kernel_timing(False)
-        # the same steps once more with no events at all (small problems are
-        # launch-bound, and the events of the timed region show up there)
+        # roofline pass: the same K steps again, the dominant class's
+        # launches bracketed by HIP events on the launch stream
+        dom = max(("xxt", "square", "rect"), key=lambda k: probe[k][0])
+        M.kernel_timing(True, classes=[dom])
         torch.cuda.synchronize()
         p0 = time.perf_counter()
         for _ in range(steps):
             one_step()
         torch.cuda.synchronize()
-        plain_ms = 1e3 * (time.perf_counter() - p0) / steps
+        events_ms = 1e3 * (time.perf_counter() - p0) / steps
+        ktime = M.read_kernel_timing()
+        M.kernel_timing(False)
 
     elapsed = t1 - t0
     nmat = sum(x.shape[0] for x in xs)
@@ -336,8 +340,8 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
         "effective_frac_of_peak": eff_tflops / PEAK_TFLOPS[cdt],
         "algorithmic_tflops": alg * steps / elapsed / 1e12,
     }
-    if plain_ms is not None:
-        rec["ms_per_step_without_events"] = plain_ms
+    if events_ms is not None:
+        rec["ms_per_step_roofline_pass"] = events_ms
     if ktime is not None:
         per = {}
         for k in ("normalize", "xxt", "square", "rect"):
@@ -365,6 +369,7 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
             avg_s = tot / cnt / 1e3
             ach = flops_per_launch / avg_s / 1e12
             rec["roofline"] = {"bound": "mfma", "kernel": f"gemm_nt_kernel ({dom})", "achieved": ach,
+                               "timed": "HIP events around each launch, roofline pass of K steps",
                                "peak": PEAK_TFLOPS[cdt], "unit": "TFLOP/s",
                                "frac": ach / PEAK_TFLOPS[cdt],
                                "traffic": recorded_traffic(workload, dom),
@@ -377,9 +382,85 @@ def run_case(name, steps, warmup, with_cpu, with_timing):
                                          "kernel": "mfma_probe_kernel (16x16x32, operands in registers)"}
                 rec["roofline"]["frac_of_loop_peak"] = ach / loop
                 rec["effective_frac_of_loop_peak"] = eff_tflops / loop
+    if with_extras and name == DEFAULT_CASE:
+        rec.update(extras(M, xs[0], outs[0], ms))
     if with_cpu:
         rec["cpu_baseline"] = cpu_baseline(wl, method)
     return rec
+
+
+def time_calls(fn, reps, warmup=2):
+    """Milliseconds per call of fn over `reps` back-to-back calls (no events;
+    synchronised on both sides)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return 1e3 * (time.perf_counter() - t0) / reps
+
+
+def extras(M, x, out, ns_ms):
+    """Comparisons the headline workload's line carries (a few seconds):
+    - syrk_unit: X X^T at 8192^2 bf16 by the triangle kernel (upper tiles,
+      mirrored), by the same kernel on every tile, and by torch.matmul
+      (hipBLASLt), as in the flash-muon excerpt on nil9.net (its symmetric
+      operator at dimension 8192 takes about half the native time);
+    - dense_products_ns: the same NS with X X^T and c A A + b A on every
+      tile, the end-to-end saving of the symmetric products (the excerpt:
+      0.71x of native NS time);
+    - gram_vs_ns: Gram NS (fp16 products, restart after step 2) against
+      standard NS (bf16 products) at alpha = 4 (the 1024 x 4096 spiked
+      workload) and alpha = 8 (the 8 x 1024 x 8192 MoE group), where
+      "Gram Newton-Schulz" §5.2 expects Gram NS to win.
+    Other hardware's figures are context, not targets."""
+    import torch
+    import synthetic as S
+    res = {}
+    x0 = x[0:1]
+    c = torch.empty((1, x.shape[1], x.shape[1]), dtype=x.dtype, device=x.device)
+    t_tri = time_calls(lambda: M.syrk_xxt(x0, out=c), 10)
+    t_full = time_calls(lambda: M.syrk_xxt(x0, out=c, full_tiles=True), 10)
+    xm, xt = x0[0], x0[0].transpose(0, 1).contiguous()
+    cm = c[0]
+    t_torch = time_calls(lambda: torch.matmul(xm, xt, out=cm), 10)
+    n, k = x.shape[1], x.shape[2]
+    res["syrk_unit"] = {
+        "shape": [int(n), int(k)], "dtype": "bf16",
+        "triangle_us": 1e3 * t_tri, "full_tiles_us": 1e3 * t_full, "torch_matmul_us": 1e3 * t_torch,
+        "triangle_over_full_tiles": t_tri / t_full, "triangle_over_torch_matmul": t_tri / t_torch,
+        "triangle_algorithmic_tflops": float(k) * n * n / (t_tri * 1e-3) / 1e12,
+        "context": "flash-muon excerpt (nil9.net): about 0.5x of native matmul at dimension 8192, "
+                   "hardware not stated"}
+    ws = torch.empty(max(M.ns_workspace_bytes(*x.shape, torch.bfloat16), 1), dtype=torch.uint8,
+                     device=x.device)
+    t_dense = time_calls(lambda: M.msign_ns(x, compute_dtype=torch.bfloat16, out=out, workspace=ws,
+                                            dense_products=True), 3, warmup=1)
+    res["dense_products_ns"] = {
+        "ms": t_dense, "symmetric_ms": ns_ms, "symmetric_over_dense": ns_ms / t_dense,
+        "context": "flash-muon excerpt (nil9.net): 0.71x end-to-end NS time, hardware not stated"}
+    cmp = {}
+    for label, workload, gi, reps in (("alpha4_1024x4096", "c2_1024x4096_bf16", 0, 50),
+                                      ("alpha8_8x1024x8192", "c5_moe_f16", 1, 10)):
+        xg = S.group_batch(S.WORKLOADS[workload].groups[gi], device=x.device)
+        yg = torch.empty_like(xg)
+        b, r, cc = xg.shape
+        wn = torch.empty(max(M.ns_workspace_bytes(b, r, cc, torch.bfloat16), 1), dtype=torch.uint8,
+                         device=x.device)
+        wg = torch.empty(max(M.gram_ns_workspace_bytes(b, r, cc, torch.float16), 1), dtype=torch.uint8,
+                         device=x.device)
+        t_ns = time_calls(lambda: M.msign_ns(xg, compute_dtype=torch.bfloat16, out=yg, workspace=wn), reps)
+        t_gr = time_calls(lambda: M.msign_gram_ns(xg, compute_dtype=torch.float16, restart_after=(2,),
+                                                  out=yg, workspace=wg), reps)
+        cmp[label] = {"shape": [int(b), int(r), int(cc)], "ns_bf16_ms": t_ns, "gram_f16_restart2_ms": t_gr,
+                      "gram_over_ns": t_gr / t_ns}
+    cmp["context"] = ("Gram Newton-Schulz §5.2: Gram NS cuts NS time by 40-50% at the aspect ratios "
+                      "of MLP and MoE weights (Kimi K2, hardware not stated)")
+    res["gram_vs_ns"] = cmp
+    return res
 
 
 def main():
@@ -403,7 +484,7 @@ def main():
                 print(f"[bench] {name}: {rec['value']:.4g} matrices/s, "
                       f"{rec['effective_tflops']:.1f} effective TFLOP/s", file=sys.stderr, flush=True)
     rec = run_case(args.case, args.steps, args.warmup, with_cpu=not args.no_cpu,
-                   with_timing=not args.no_timing)
+                   with_timing=not args.no_timing, with_extras=not args.no_extras)
     print(json.dumps(rec), flush=True)
 
 

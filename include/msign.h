@@ -92,7 +92,13 @@ size_t msign_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
  *   compute_dtype  operand dtype of the matrix products: MSIGN_BF16 or
  *                  MSIGN_F16 (MFMA with fp32 accumulation) or MSIGN_F32 (fp32
  *                  MFMA).  The iterate X itself is carried in fp32 between
- *                  steps; A and B are stored in compute_dtype.
+ *                  steps; A and B are stored in compute_dtype.  Matrices
+ *                  with n = min(rows, cols) <= 64 fit one 64-wide tile, where
+ *                  the iteration is bound by launch latency: their products
+ *                  always run in fp32 (no slower; 16-bit operands would miss
+ *                  2e-2 on vector-like inputs, where a_t + b_t + c_t is a
+ *                  cancellation).  In a grouped call such matrices form an
+ *                  fp32 sub-call of their own.
  *   steps          1..MSIGN_MAX_STEPS.
  *   coeffs         HOST pointer to steps*3 floats (a_t, b_t, c_t per row,
  *                  [KX] §解开约束), or NULL for (3.4445, -4.7750, 2.0315)
@@ -120,9 +126,19 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows,
  *       s = (sum A2^2 + eps)^(1/8) = ||(X0 X0^T)^2||_F^(1/4) <= ||X0||_F,
  *       i.e. X1 = a X0/s + (b A/s^2 + c A2/s^4) X0/s.  A2 is formed even when
  *       c_1 = 0.  Later steps are unchanged.
- *   Other bits are MSIGN_ERR_ARG.
  */
 #define MSIGN_NS_IMPROVED_INIT 1u
+/*
+ *   MSIGN_NS_DENSE_PRODUCTS  measurement comparator: X X^T and c A A + b A
+ *       are computed on every tile (plain products, no triangle), so their
+ *       cost can be set against the triangle products' ([NB] flash-muon:
+ *       the symmetric X X^T operator and its end-to-end NS saving).  Same
+ *       arithmetic per element; the stored A and B are then symmetric only
+ *       up to rounding.  One non-empty group only; not with
+ *       MSIGN_NS_IMPROVED_INIT (MSIGN_ERR_ARG).
+ *   Other bits are MSIGN_ERR_ARG.
+ */
+#define MSIGN_NS_DENSE_PRODUCTS 2u
 msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows,
                            int64_t cols, int32_t io_dtype, int32_t compute_dtype,
                            int32_t steps, const float* coeffs, float eps,
@@ -148,7 +164,8 @@ size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
  * first Q of each block is Z + a_t I, added on the diagonal in registers.
  *
  *   compute_dtype   MSIGN_F16 (the pages' choice, [GR] §3.3), MSIGN_BF16 or
- *                   MSIGN_F32.
+ *                   MSIGN_F32; as in msign_ns, matrices with n <= 64 always
+ *                   use fp32 products.
  *   restart_after   HOST array of n_restarts step indices, strictly
  *                   increasing, each in 1..steps-1; NULL iff n_restarts == 0.
  *                   Algorithm 2 uses {2}.
@@ -285,6 +302,18 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n,
                         int64_t k, int32_t dtype, float alpha, const void* d,
                         float beta, float gamma, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * syrk_xxt_ex - syrk_xxt with option flags (flags = 0 is syrk_xxt).
+ *   MSIGN_SYRK_FULL_TILES  measurement comparator: every tile of X X^T is
+ *       computed (a plain product, no triangle) and C is symmetric only up
+ *       to rounding.  Same workspace rules as syrk_xxt.
+ *   Other bits are MSIGN_ERR_ARG.
+ */
+#define MSIGN_SYRK_FULL_TILES 1u
+msign_status_t syrk_xxt_ex(const void* x, void* c, int64_t batch, int64_t n, int64_t k, int32_t dtype,
+                           float alpha, const void* d, float beta, float gamma, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 const char* msign_status_string(msign_status_t status);

@@ -76,6 +76,8 @@ def _load():
     lib.msign_gram_ns.restype = ctypes.c_int
     lib.syrk_xxt.argtypes = [vp, vp, i64, i64, i64, i32, f, vp, f, f, vp, sz, vp]
     lib.syrk_xxt.restype = ctypes.c_int
+    lib.syrk_xxt_ex.argtypes = [vp, vp, i64, i64, i64, i32, f, vp, f, f, ctypes.c_uint32, vp, sz, vp]
+    lib.syrk_xxt_ex.restype = ctypes.c_int
     gp = ctypes.POINTER(_Group)
     lib.msign_ns_grouped_workspace_bytes.argtypes = [gp, i32, i32]
     lib.msign_ns_grouped_workspace_bytes.restype = sz
@@ -180,16 +182,19 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
 
 
 IMPROVED_INIT = 1  # MSIGN_NS_IMPROVED_INIT
+DENSE_PRODUCTS = 2  # MSIGN_NS_DENSE_PRODUCTS
+SYRK_FULL_TILES = 1  # MSIGN_SYRK_FULL_TILES
 
 
 def msign_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-20,
              compute_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None,
-             improved_init: bool = False) -> torch.Tensor:
+             improved_init: bool = False, dense_products: bool = False) -> torch.Tensor:
     """Standard quintic Newton-Schulz msign over the last two dims (C ABI
-    `msign_ns`, or `msign_ns_ex` with MSIGN_NS_IMPROVED_INIT when
-    `improved_init`).  `coeffs`: None (Keller constants), one (a, b, c) triple
-    or a table of `steps` rows.  Returns a tensor shaped and typed like `x`."""
+    `msign_ns_ex`, with MSIGN_NS_IMPROVED_INIT when `improved_init` and the
+    full-tile comparator MSIGN_NS_DENSE_PRODUCTS when `dense_products`).
+    `coeffs`: None (Keller constants), one (a, b, c) triple or a table of
+    `steps` rows.  Returns a tensor shaped and typed like `x`."""
     _check_cuda(x, out, workspace)
     lib = _load()
     x = x.contiguous()
@@ -203,7 +208,8 @@ def msign_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-20,
     carr = _coeff_array(coeffs, steps)
     with torch.cuda.device(x.device):
         st = lib.msign_ns_ex(x.data_ptr(), y.data_ptr(), batch, rows, cols, io, cdt, steps,
-                             carr, float(eps), IMPROVED_INIT if improved_init else 0,
+                             carr, float(eps),
+                             (IMPROVED_INIT if improved_init else 0) | (DENSE_PRODUCTS if dense_products else 0),
                              ws.data_ptr(), ws.numel(), _stream_handle(x.device))
     _check(st)
     return y
@@ -366,9 +372,11 @@ def mfma_probe(iters: int, dtype=torch.bfloat16, device="cuda", out: Optional[to
 
 def syrk_xxt(x: torch.Tensor, alpha: float = 1.0, d: Optional[torch.Tensor] = None,
              beta: float = 0.0, gamma: float = 0.0,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, full_tiles: bool = False) -> torch.Tensor:
     """C = alpha X X^T + beta D + gamma I over the last two dims (C ABI
-    `syrk_xxt`); C is exactly symmetric."""
+    `syrk_xxt`; `syrk_xxt_ex` with MSIGN_SYRK_FULL_TILES when `full_tiles`,
+    the plain-product comparator).  C is exactly symmetric unless
+    `full_tiles`."""
     _check_cuda(x, d, out)
     lib = _load()
     x = x.contiguous()
@@ -389,10 +397,11 @@ def syrk_xxt(x: torch.Tensor, alpha: float = 1.0, d: Optional[torch.Tensor] = No
     if nbytes > 0:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     with torch.cuda.device(x.device):
-        st = lib.syrk_xxt(x.data_ptr(), c.data_ptr(), batch, n, k, dt, float(alpha),
-                          d.data_ptr() if d is not None else None, float(beta), float(gamma),
-                          ws.data_ptr() if ws is not None else None, nbytes,
-                          _stream_handle(x.device))
+        st = lib.syrk_xxt_ex(x.data_ptr(), c.data_ptr(), batch, n, k, dt, float(alpha),
+                             d.data_ptr() if d is not None else None, float(beta), float(gamma),
+                             SYRK_FULL_TILES if full_tiles else 0,
+                             ws.data_ptr() if ws is not None else None, nbytes,
+                             _stream_handle(x.device))
     _check(st)
     return c
 

@@ -35,4 +35,11 @@ hipError_t launch_products_single(int32_t cdt, bool tri, const GemmParams* qs, c
 hipError_t launch_products_grouped(int32_t cdt, bool tri, const GemmParams* qs, const GroupPlan& l,
                                    hipStream_t st);
 
+// Full-tile product of one problem with both operands read along K: every
+// tile of P Q^T is computed (no triangle), for measuring the triangle
+// kernels against the plain product.  Outputs of a symmetric result should
+// be given as transposed stores (the same matrix), which take the staged
+// whole-line epilogue.
+hipError_t launch_products_dense(int32_t cdt, const GemmParams* qs, const GroupPlan& l, hipStream_t st);
+
 }  // namespace msign

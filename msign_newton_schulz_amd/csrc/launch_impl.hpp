@@ -65,6 +65,14 @@ hipError_t launch_at(const GemmParams* qs, const GroupPlan& l, hipStream_t st) {
   return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, true, NG>(qs, l, st);
 }
 
+// Full-tile products with both operands row-major along K (single problems).
+template <typename T>
+hipError_t launch_dense(const GemmParams* qs, const GroupPlan& l, hipStream_t st) {
+  if (l.bm == 256) return launch_cfg<T, 256, 256, 4, 4, 128, 0, false, 1, false, 1>(qs, l, st);
+  if (l.bm == 128) return launch_cfg<T, 128, 128, 2, 2, 64, 0, false, 1, false, 1>(qs, l, st);
+  return launch_cfg<T, 64, 64, 1, 1, 64, 2, false, 4, false, 1>(qs, l, st);
+}
+
 template <int NG>
 hipError_t launch_products(int32_t cdt, bool tri, const GemmParams* qs, const GroupPlan& l, hipStream_t st) {
   switch (cdt) {

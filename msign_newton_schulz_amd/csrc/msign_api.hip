@@ -344,7 +344,9 @@ static_assert(kMaxGroups == MSIGN_MAX_GROUPS, "group table size");
 // K, P == Q symmetric or P Q^T symmetric) or a rectangular one with P stored
 // K-major.  `partial`/`partial_cap` is workspace for the K-split tail; with
 // too little of it the tail is computed whole instead.
-enum ProductKind { TRIANGLE, RECT_KMAJOR };
+// DENSE: every tile of P Q^T with both operands read along K (the
+// measurement comparator of the triangle products; one group only).
+enum ProductKind { TRIANGLE, RECT_KMAJOR, DENSE };
 
 Dims dims_of(const GemmParams& q, int64_t batch) { return Dims{q.M, q.N, q.K, batch}; }
 
@@ -360,6 +362,7 @@ hipError_t launch_grouped(int32_t cdt, ProductKind kind, GemmParams* qs, const i
   }
   for (int i = 0; i < ng; ++i) qs[i].partial = static_cast<float*>(partial);
   if (used) *used = l;
+  if (kind == DENSE) return launch_products_dense(cdt, qs, l, st);
   return ng == 1 ? launch_products_single(cdt, tri, qs, l, st) : launch_products_grouped(cdt, tri, qs, l, st);
 }
 
@@ -585,6 +588,44 @@ msign_status_t check_call_ws(const Prob* pr, int ng, int32_t io_dtype, void* ws,
   return MSIGN_OK;
 }
 
+// Matrices with n <= 64 fit one 64-wide tile along n.  Their iteration is
+// bound by launch latency, not by the products, so their products run in
+// fp32 whatever the compute dtype: at no cost in time, and with 16-bit
+// operands the iteration misses its tolerance on vector-like inputs (a 1 x m
+// matrix is the scalar map x <- (a + b + c) x at x = 1, where a + b + c =
+// 0.70 is a cancellation of 3.44 against -2.74 that magnifies the rounding
+// of B).
+constexpr int64_t kFp32MaxN = 64;
+
+// The problems of a call, split by the dtype their products use: sub-call 0
+// in the compute dtype, sub-call 1 (n <= 64) in fp32, each a grouped call of
+// its own with its own workspace region (sub-call 0's first).
+struct SubCalls {
+  int n[2];
+  Prob p[2][MSIGN_MAX_GROUPS];
+  int32_t cdt[2];
+  size_t off[2], total;
+};
+
+template <typename P, typename F>
+SubCalls split_call(const Prob* pr, int ng, int32_t cdt, F regions) {
+  SubCalls sc;
+  sc.n[0] = sc.n[1] = 0;
+  sc.cdt[0] = cdt;
+  sc.cdt[1] = MSIGN_F32;
+  for (int i = 0; i < ng; ++i) {
+    const int k = (cdt != MSIGN_F32 && pr[i].s.n <= kFp32MaxN) ? 1 : 0;
+    sc.p[k][sc.n[k]++] = pr[i];
+  }
+  size_t off = 0;
+  for (int k = 0; k < 2; ++k) {
+    sc.off[k] = off;
+    if (sc.n[k] > 0) off = align256(off + plan_call<P>(sc.p[k], sc.n[k], sc.cdt[k], regions).total);
+  }
+  sc.total = off;
+  return sc;
+}
+
 size_t call_workspace(const msign_group_t* groups, int32_t ngroups, int32_t cdt, bool gram) {
   if (ngroups < 1 || ngroups > MSIGN_MAX_GROUPS || !groups || !dt_valid(cdt)) return (size_t)-1;
   Prob pr[MSIGN_MAX_GROUPS];
@@ -599,27 +640,20 @@ size_t call_workspace(const msign_group_t* groups, int32_t ngroups, int32_t cdt,
     p.s = canon(g.rows, g.cols);
   }
   if (ng == 0) return 0;
-  return gram ? plan_call<GramPlan>(pr, ng, cdt, plan_gram_regions).total
-              : plan_call<NsPlan>(pr, ng, cdt, plan_ns_regions).total;
+  return gram ? split_call<GramPlan>(pr, ng, cdt, plan_gram_regions).total
+              : split_call<NsPlan>(pr, ng, cdt, plan_ns_regions).total;
 }
 
-// Standard NS over ng problems: every product is one launch over all of
-// them (a grouped launch), the normalise passes run per problem.
-msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
-                      int32_t steps, const float* coeffs, float eps, uint32_t flags, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
-  if (flags & ~(uint32_t)MSIGN_NS_IMPROVED_INIT) return fail(MSIGN_ERR_ARG, "unknown flag");
-  const bool improved = (flags & MSIGN_NS_IMPROVED_INIT) != 0;
-  Prob pr[MSIGN_MAX_GROUPS];
-  int ng = 0;
-  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
-  if (st != MSIGN_OK || ng == 0) return st;
-  const CallPlan<NsPlan> cp = plan_call<NsPlan>(pr, ng, compute_dtype, plan_ns_regions);
-  st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, cp.total);
-  if (st != MSIGN_OK) return st;
+// The launches of standard NS over checked problems pr[0..ng), all of whose
+// products use compute dtype `cdt`, in a workspace laid out by plan_call.
+msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, int32_t steps, const float* coeffs,
+                       float eps, bool improved, bool dense, void* workspace, hipStream_t stream) {
+  // symmetric n x n results: triangle products, or (dense) every tile with
+  // the result stored through its transpose, the same matrix
+  const ProductKind sym = dense ? DENSE : TRIANGLE;
+  const CallPlan<NsPlan> cp = plan_call<NsPlan>(pr, ng, cdt, plan_ns_regions);
+  msign_status_t st = MSIGN_OK;
 
-  const int32_t cdt = compute_dtype;
   void* split = at(workspace, cp.split);
   struct G {
     Shape s;
@@ -665,10 +699,10 @@ msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_d
       for (int i = 0; i < ng; ++i) {
         const G& v = gv[i];
         qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
-        add_out(qs[i], v.A, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+        add_out(qs[i], v.A, v.s.np, v.nn, cdt, dense, v.s.np, v.s.np, 0.f, 0, true);
       }
       TimedLaunch tl(KC_SYRK, stream);
-      e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes);
+      e = launch_grouped(cdt, sym, qs, batches, ng, stream, split, cp.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "X X^T");
     }
     // Improved initial normalisation (§改良初值), first step only: A2 = A A
@@ -714,10 +748,10 @@ msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_d
         const G& v = gv[i];
         qs[i] = gemm_base(v.A, v.s.np, v.nn, v.A, v.s.np, v.nn, v.s.np, v.s.np, v.s.np, c);
         set_d(qs[i], v.A, v.s.np, v.nn, cdt, b, true);
-        add_out(qs[i], v.B, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
+        add_out(qs[i], v.B, v.s.np, v.nn, cdt, dense, v.s.np, v.s.np, 0.f, 0, true);
       }
       TimedLaunch tl(KC_SQUARE, stream);
-      e = launch_grouped(cdt, TRIANGLE, qs, batches, ng, stream, split, cp.split_bytes);
+      e = launch_grouped(cdt, sym, qs, batches, ng, stream, split, cp.split_bytes);
       if (e != hipSuccess) return hip_fail(e, "c A A + b A");
     }
     {  // X' = B X + a X, as C' = X^T B + a X^T (m x n) with X read K-major;
@@ -744,6 +778,35 @@ msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_d
   return MSIGN_OK;
 }
 
+// Standard NS over ng problems: every product is one launch over all of
+// them (a grouped launch), the normalise passes run per problem.  Arguments
+// are checked; each sub-call (see split_call) runs with its own dtype.
+msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
+                      int32_t steps, const float* coeffs, float eps, uint32_t flags, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (flags & ~(uint32_t)(MSIGN_NS_IMPROVED_INIT | MSIGN_NS_DENSE_PRODUCTS)) return fail(MSIGN_ERR_ARG, "unknown flag");
+  const bool improved = (flags & MSIGN_NS_IMPROVED_INIT) != 0;
+  const bool dense = (flags & MSIGN_NS_DENSE_PRODUCTS) != 0;
+  if (dense && improved)
+    return fail(MSIGN_ERR_ARG, "MSIGN_NS_DENSE_PRODUCTS does not combine with MSIGN_NS_IMPROVED_INIT");
+  Prob pr[MSIGN_MAX_GROUPS];
+  int ng = 0;
+  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+  if (st != MSIGN_OK || ng == 0) return st;
+  if (dense && ng > 1) return fail(MSIGN_ERR_ARG, "MSIGN_NS_DENSE_PRODUCTS takes one non-empty group");
+  const SubCalls sc = split_call<NsPlan>(pr, ng, compute_dtype, plan_ns_regions);
+  st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, sc.total);
+  if (st != MSIGN_OK) return st;
+  for (int k = 0; k < 2; ++k) {
+    if (sc.n[k] == 0) continue;
+    st = ns_exec(sc.p[k], sc.n[k], io_dtype, sc.cdt[k], steps, coeffs, eps, improved, dense,
+                 at(workspace, sc.off[k]), stream);
+    if (st != MSIGN_OK) return st;
+  }
+  return MSIGN_OK;
+}
+
 // Restart list of Gram NS: strictly increasing step indices in 1..steps-1
 // (steps itself is checked with the other arguments).
 msign_status_t parse_restarts(int32_t steps, const int32_t* restart_after, int32_t n_restarts, bool* restart_at) {
@@ -762,23 +825,14 @@ msign_status_t parse_restarts(int32_t steps, const int32_t* restart_after, int32
   return MSIGN_OK;
 }
 
-// Gram NS over ng problems, every product one grouped launch.
-msign_status_t gram_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
-                        int32_t steps, const float* coeffs, float eps, const int32_t* restart_after,
-                        int32_t n_restarts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  g_err.clear();
-  bool restart_at[MSIGN_MAX_STEPS + 1] = {false};
-  msign_status_t st0 = parse_restarts(steps, restart_after, n_restarts, restart_at);
-  if (st0 != MSIGN_OK) return st0;
-  Prob pr[MSIGN_MAX_GROUPS];
-  int ng = 0;
-  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
-  if (st != MSIGN_OK || ng == 0) return st;
-  const CallPlan<GramPlan> cp = plan_call<GramPlan>(pr, ng, compute_dtype, plan_gram_regions);
-  st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, cp.total);
-  if (st != MSIGN_OK) return st;
-
-  const int32_t cdt = compute_dtype;
+// The launches of Gram NS over checked problems pr[0..ng) with products in
+// `cdt`, in a workspace laid out by plan_call; restart_at[t] marks a
+// restart after step t.
+msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, int32_t steps,
+                         const float* coeffs, float eps, const bool* restart_at, void* workspace,
+                         hipStream_t stream) {
+  const CallPlan<GramPlan> cp = plan_call<GramPlan>(pr, ng, cdt, plan_gram_regions);
+  msign_status_t st = MSIGN_OK;
   void* split = at(workspace, cp.split);
   struct G {
     Shape s;
@@ -882,6 +936,31 @@ msign_status_t gram_run(const msign_group_t* groups, int32_t ngroups, int32_t io
     }
   }
   return apply_q(true, "y = Q X");  // y = Q X
+}
+
+// Gram NS over ng problems, every product one grouped launch; arguments
+// checked here, each sub-call (see split_call) run with its own dtype.
+msign_status_t gram_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
+                        int32_t steps, const float* coeffs, float eps, const int32_t* restart_after,
+                        int32_t n_restarts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  bool restart_at[MSIGN_MAX_STEPS + 1] = {false};
+  msign_status_t st0 = parse_restarts(steps, restart_after, n_restarts, restart_at);
+  if (st0 != MSIGN_OK) return st0;
+  Prob pr[MSIGN_MAX_GROUPS];
+  int ng = 0;
+  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+  if (st != MSIGN_OK || ng == 0) return st;
+  const SubCalls sc = split_call<GramPlan>(pr, ng, compute_dtype, plan_gram_regions);
+  st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, sc.total);
+  if (st != MSIGN_OK) return st;
+  for (int k = 0; k < 2; ++k) {
+    if (sc.n[k] == 0) continue;
+    st = gram_exec(sc.p[k], sc.n[k], io_dtype, sc.cdt[k], steps, coeffs, eps, restart_at,
+                   at(workspace, sc.off[k]), stream);
+    if (st != MSIGN_OK) return st;
+  }
+  return MSIGN_OK;
 }
 
 // ------------------------------------------------------------ Muon step --
@@ -1132,7 +1211,15 @@ size_t syrk_xxt_workspace_bytes(int64_t batch, int64_t n, int64_t k, int32_t dty
 msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_t k, int32_t dtype,
                         float alpha, const void* d, float beta, float gamma, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
+  return syrk_xxt_ex(x, c, batch, n, k, dtype, alpha, d, beta, gamma, 0u, workspace, workspace_bytes, stream);
+}
+
+msign_status_t syrk_xxt_ex(const void* x, void* c, int64_t batch, int64_t n, int64_t k, int32_t dtype,
+                           float alpha, const void* d, float beta, float gamma, uint32_t flags,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
+  if (flags & ~(uint32_t)MSIGN_SYRK_FULL_TILES) return fail(MSIGN_ERR_ARG, "unknown flag");
+  const bool full = (flags & MSIGN_SYRK_FULL_TILES) != 0;
   if (!dt_valid(dtype)) return fail(MSIGN_ERR_DTYPE, "dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
   if (batch < 0 || n < 0 || k < 0) return fail(MSIGN_ERR_SHAPE, "batch, n and k must be >= 0");
   if (batch > kMaxBatch) return fail(MSIGN_ERR_SHAPE, "batch must be <= 65535");
@@ -1197,9 +1284,11 @@ msign_status_t syrk_xxt(const void* x, void* c, int64_t batch, int64_t n, int64_
   GemmParams g = gemm_base(P, ldp, sp, P, ldp, sp, n, n, K, alpha);
   const bool vec_c = (n % 4 == 0) && aligned(c, 4 * es);
   if (d && beta != 0.f) set_d(g, d, n, n * n, dtype, beta, (n % 4 == 0) && aligned(d, 4 * es));
-  add_out(g, c, n, n * n, dtype, false, n, n, gamma, n, vec_c);
+  // full tiles: C is stored through its transpose (the same matrix), which
+  // takes the whole-line epilogue when there is no diagonal term
+  add_out(g, c, n, n * n, dtype, full, n, n, gamma, gamma != 0.f ? n : 0, vec_c);
   TimedLaunch tl(KC_SYRK, stream);
-  hipError_t e = launch_nt(dtype, TRIANGLE, g, batch, stream, split, split_cap);
+  hipError_t e = launch_nt(dtype, full ? DENSE : TRIANGLE, g, batch, stream, split, split_cap);
   if (e != hipSuccess) return hip_fail(e, "syrk_xxt");
   return MSIGN_OK;
 }

@@ -117,10 +117,15 @@ def test_ns_argument_errors_before_launch():
 def test_ns_ex_rejects_unknown_flags():
     lib = _lib()
     args = (FAKE, FAKE, 1, 8, 16, 1, 1, 5, None, 1e-20)
-    assert lib.msign_ns_ex(*args, 2, FAKE2, 1 << 30, None) == 1
+    assert lib.msign_ns_ex(*args, 4, FAKE2, 1 << 30, None) == 1
     assert lib.msign_ns_ex(*args, 0x80000000, FAKE2, 1 << 30, None) == 1
+    # the dense-products comparator does not combine with the improved init
+    assert lib.msign_ns_ex(*args, 3, FAKE2, 1 << 30, None) == 1
     # a valid flag still goes through the other checks (too small a workspace)
     assert lib.msign_ns_ex(*args, 1, FAKE2, 16, None) == 4
+    assert lib.msign_ns_ex(*args, 2, FAKE2, 16, None) == 4
+    # syrk_xxt_ex: one flag (full tiles); others rejected before any launch
+    assert lib.syrk_xxt_ex(FAKE, FAKE2, 1, 8, 64, 1, 1.0, None, 0.0, 0.0, 2, None, 0, None) == 1
 
 
 def _gram(lib, restarts, n_restarts, steps=5, **kw):

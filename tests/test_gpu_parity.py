@@ -69,6 +69,27 @@ def test_syrk_fused_epilogue(dt):
     assert torch.equal(c, c.transpose(-1, -2).contiguous())
 
 
+@pytest.mark.parametrize("n,k,batch", [(100, 300, 2), (1536, 1024, 2), (2048, 2048, 4)])
+def test_syrk_full_tiles_comparator(n, k, batch):
+    """The full-tile comparator (every tile of X X^T, the three tile tiers)
+    within the product's error bound, and equal to the triangle kernel's
+    result up to the same bound."""
+    M = require_gpu()
+    announce(f"syrk full tiles n={n} k={k} batch={batch}")
+    x = _input(n, k, "bf16", 600 + n, batch=batch)
+    xc = x.cuda()
+    c = M.syrk_xxt(xc, full_tiles=True)
+    t = M.syrk_xxt(xc)
+    torch.cuda.synchronize()
+    for i in sorted({0, batch - 1}):
+        xx = f64(x[i])
+        ref = xx @ xx.T
+        scale = np.abs(xx) @ np.abs(xx).T
+        bound = scale * (2.0 ** -8 + 2 * k * 2.0 ** -24)
+        assert np.all(np.abs(f64(c[i]) - ref) <= bound)
+        assert np.all(np.abs(f64(c[i]) - f64(t[i])) <= 2 * bound)
+
+
 def test_syrk_deterministic_and_batched_matches_single():
     M = require_gpu()
     announce("syrk determinism")
@@ -107,8 +128,12 @@ NS_CASES = [
     (200, 70, "bf16", "bf16", 2),   # tall, ragged
     (70, 200, "bf16", "bf16", 2),   # wide, ragged
     (129, 129, "bf16", "f16", 1),   # square, ragged tail
-    (1, 37, "bf16", "f16", 1),      # a vector
+    (1, 37, "bf16", "bf16", 1),     # a vector (n <= 64: fp32 products)
+    (1, 37, "bf16", "f16", 1),
     (37, 1, "f16", "f16", 1),
+    (37, 1, "bf16", "bf16", 2),
+    (64, 300, "bf16", "bf16", 2),   # n = 64, the largest fp32-product size
+    (65, 300, "bf16", "bf16", 1),   # n = 65, the smallest bf16-product size
     (96, 160, "f16", "bf16", 3),
     (300, 520, "f32", "f32", 1),
 ]
@@ -126,22 +151,44 @@ def test_ns_matches_oracle(rows, cols, io, cdt, batch):
     assert err <= TOL[cdt], err
 
 
-def test_ns_vector_bf16_precision_limit():
-    """A 1 x m input in bf16 products.  The iteration is then scalar:
-    x <- a x + B x with B = b + c at x = 1, and the output a + B = 0.70 is a
-    cancellation of 3.44 and -2.74.  Rounding B to bf16 (relative 2^-9 of
-    2.74) perturbs each step by about 2^-9 * 2.74 / 0.70 = 0.8%, plus 0.2%
-    for the operand X, so five steps stay within about 5%: above the 2e-2
-    target, which bf16 products cannot reach on this input."""
+def test_ns_tiny_n_runs_fp32_products():
+    """n <= 64 runs its products in fp32 whatever compute_dtype: a bf16 call
+    gives the bits of the fp32 call, in a grouped call too (its own sub-call
+    next to the bf16 group), and reaches the fp32 tolerance before the
+    output's own bf16 rounding."""
     M = require_gpu()
-    announce("msign_ns 1x37 bf16 precision limit")
-    x = _input(1, 37, "bf16", 1000 + 7 + 37)
-    y = M.msign_ns(x.cuda(), compute_dtype=torch.bfloat16)
+    announce("msign_ns n <= 64 fp32 products")
+    x = _input(48, 200, "f32", 4711, batch=2)
+    big = _input(96, 200, "f32", 4712, batch=1)
+    y_bf = M.msign_ns(x.cuda(), compute_dtype=torch.bfloat16)
+    y_32 = M.msign_ns(x.cuda(), compute_dtype=torch.float32)
+    y_grp, y_big = M.msign_ns_grouped([x.cuda(), big.cuda()], compute_dtype=torch.bfloat16)
+    y_big1 = M.msign_ns(big.cuda(), compute_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    a, b, c = O.KELLER_ABC
-    per_step = 2.0 ** -9 * (abs(b + c) / abs(a + b + c) + 1.0)
-    err = O.max_rel_fro_error(f64(y), O.ns(f64(x)))
-    assert err <= 5 * per_step, (err, 5 * per_step)
+    assert torch.equal(y_bf, y_32)
+    assert torch.equal(y_grp, y_32)
+    assert torch.equal(y_big, y_big1)
+    assert O.max_rel_fro_error(f64(y_bf), O.ns(f64(x))) <= 1e-4
+
+
+@pytest.mark.parametrize("rows,cols,batch,cdt", [
+    (160, 352, 2, "bf16"),     # 64 x 64 tiles
+    (1536, 1536, 2, "bf16"),   # 128 x 128 tiles
+    (2048, 2048, 4, "bf16"),   # 256 x 256 tiles
+    (200, 96, 1, "f32"),       # tall, fp32 products
+])
+def test_ns_dense_products_comparator(rows, cols, batch, cdt):
+    """NS with X X^T and c A A + b A on every tile (the measurement
+    comparator of the triangle products) matches the oracle like the
+    symmetric path does."""
+    M = require_gpu()
+    announce(f"msign_ns dense products {batch}x{rows}x{cols} compute={cdt}")
+    x = _input(rows, cols, "f32" if cdt == "f32" else "bf16", 700 + rows, batch=batch)
+    y = M.msign_ns(x.cuda(), compute_dtype=TORCH_DT[cdt], dense_products=True)
+    torch.cuda.synchronize()
+    for i in sorted({0, batch - 1}):
+        err = O.max_rel_fro_error(f64(y[i]), O.ns(f64(x[i])))
+        assert err <= TOL[cdt], (i, err)
 
 
 def test_ns_small_fp32_workload_against_exact_and_oracle():
@@ -309,6 +356,8 @@ GRAM_CASES = [
     (130, 260, "f16", "f16", (), 1),
     (130, 260, "bf16", "bf16", (2,), 1),
     (1, 40, "f16", "f16", (2,), 1),
+    (1, 40, "bf16", "bf16", (2,), 1),    # n <= 64: fp32 products
+    (40, 1, "bf16", "bf16", (), 2),
 ]
 
 
