@@ -145,6 +145,33 @@ msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows,
                            uint32_t flags, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * msign_ns_noalloc - msign_ns without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same computation, kernels and
+ * results (bit for bit) as msign_ns with the same arguments.
+ *
+ * Its workspace is a fixed scratch array of MSIGN_NOALLOC_SCRATCH_BYTES that
+ * the library holds in device memory, one per device it runs on, until the
+ * process ends; its device address is looked up once per device, on the
+ * first call with that device current.  The call allocates and frees
+ * nothing and creates no events (kernel timing does not apply to it).
+ *   - A problem whose msign_ns_workspace_bytes(...) exceeds
+ *     MSIGN_NOALLOC_SCRATCH_BYTES gets MSIGN_ERR_WORKSPACE, nothing launched
+ *     (e.g. 1 x 1024 x 4096 bf16 fits; 1 x 2048 x 4096 does not).
+ *   - Nothing in the scratch must start at zero: every region is written
+ *     before it is read, so the contents a previous call left are harmless.
+ *   - All calls on one device share its scratch: calls that may overlap in
+ *     time on one device (different streams, or host threads without
+ *     ordering) race and give wrong results.  Order them on one stream.
+ *   - Other arguments, errors and aliasing rules as msign_ns.
+ */
+#define MSIGN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+msign_status_t msign_ns_noalloc(const void* x, void* y, int64_t batch, int64_t rows,
+                                int64_t cols, int32_t io_dtype, int32_t compute_dtype,
+                                int32_t steps, const float* coeffs, float eps,
+                                hipStream_t stream);
+
 /* Bytes of device workspace msign_gram_ns needs; see msign_ns_workspace_bytes. */
 size_t msign_gram_ns_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
                                      int32_t compute_dtype);

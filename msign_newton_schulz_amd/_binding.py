@@ -72,6 +72,8 @@ def _load():
     lib.msign_ns.restype = ctypes.c_int
     lib.msign_ns_ex.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, fp, f, ctypes.c_uint32, vp, sz, vp]
     lib.msign_ns_ex.restype = ctypes.c_int
+    lib.msign_ns_noalloc.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, fp, f, vp]
+    lib.msign_ns_noalloc.restype = ctypes.c_int
     lib.msign_gram_ns.argtypes = [vp, vp, i64, i64, i64, i32, i32, i32, fp, f, ip, i32, vp, sz, vp]
     lib.msign_gram_ns.restype = ctypes.c_int
     lib.syrk_xxt.argtypes = [vp, vp, i64, i64, i64, i32, f, vp, f, f, vp, sz, vp]
@@ -213,6 +215,30 @@ def msign_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-20,
                              ws.data_ptr(), ws.numel(), _stream_handle(x.device))
     _check(st)
     return y
+
+
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024  # MSIGN_NOALLOC_SCRATCH_BYTES
+
+
+def msign_ns_noalloc(x: torch.Tensor, out: torch.Tensor, steps: int = 5, coeffs=None,
+                     eps: float = 1e-20, compute_dtype=torch.bfloat16) -> torch.Tensor:
+    """msign_ns through the allocation-free entry point (C ABI
+    `msign_ns_noalloc`): the library's fixed per-device scratch replaces the
+    workspace, so nothing is allocated; `out` must be given.  Calls that may
+    overlap in time on one device race on that scratch."""
+    _check_cuda(x, out)
+    lib = _load()
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (a copy would allocate)")
+    batch, rows, cols = _batch_dims(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous with the shape and dtype of x")
+    carr = _coeff_array(coeffs, steps)
+    with torch.cuda.device(x.device):
+        st = lib.msign_ns_noalloc(x.data_ptr(), out.data_ptr(), batch, rows, cols, _dt(x.dtype),
+                                  _dt(compute_dtype), steps, carr, float(eps), _stream_handle(x.device))
+    _check(st)
+    return out
 
 
 def msign_gram_ns(x: torch.Tensor, steps: int = 5, coeffs=None, eps: float = 1e-20,

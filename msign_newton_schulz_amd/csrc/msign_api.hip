@@ -199,13 +199,17 @@ hipEvent_t pool_event(Timing& t) {
 }
 
 // Brackets one launch with events when timing is enabled.
+// Set while a call that may allocate nothing runs on this thread: its
+// launches are never bracketed by (created) events.
+thread_local bool g_untimed = false;
+
 struct TimedLaunch {
   int kclass;
   hipStream_t stream;
   hipEvent_t start = nullptr, stop = nullptr;
   TimedLaunch(int kc, hipStream_t s) : kclass(kc), stream(s) {
     Timing& t = timing();
-    if (!((t.mask.load() >> kc) & 1u)) return;
+    if (g_untimed || !((t.mask.load() >> kc) & 1u)) return;
     std::lock_guard<std::mutex> g(t.mu);
     start = pool_event(t);
     stop = pool_event(t);
@@ -1104,6 +1108,40 @@ msign_status_t muon_run(const muon_group_t* groups, int32_t ngroups, int32_t io_
   return MSIGN_OK;
 }
 
+// ------------------------------------------------- allocation-free calls --
+
+// Scratch of msign_ns_noalloc, for callers that cannot allocate device
+// memory.  Each device the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is
+// passed to kernels.
+static_assert(MSIGN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[MSIGN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device).
+msign_status_t device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSIGN_ERR_HIP, "device index out of range");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256)) return fail(MSIGN_ERR_HIP, "scratch address is null or misaligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSIGN_OK;
+}
+
 msign_group_t one_group(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols) {
   msign_group_t g;
   g.x = x; g.y = y; g.batch = batch; g.rows = rows; g.cols = cols;
@@ -1138,6 +1176,32 @@ msign_status_t msign_ns(const void* x, void* y, int64_t batch, int64_t rows, int
                         float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const msign_group_t g = one_group(x, y, batch, rows, cols);
   return ns_run(&g, 1, io_dtype, compute_dtype, steps, coeffs, eps, 0u, workspace, workspace_bytes, stream);
+}
+
+msign_status_t msign_ns_noalloc(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
+                                int32_t io_dtype, int32_t compute_dtype, int32_t steps, const float* coeffs,
+                                float eps, hipStream_t stream) {
+  g_err.clear();
+  const msign_group_t g = one_group(x, y, batch, rows, cols);
+  {  // the argument checks of msign_ns, before the device is touched
+    Prob pr[1];
+    int ng = 0;
+    msign_status_t st = gather(&g, 1, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+    if (st != MSIGN_OK || ng == 0) return st;
+  }
+  const size_t need = call_workspace(&g, 1, compute_dtype, false);
+  if (need == (size_t)-1) return fail(MSIGN_ERR_SHAPE, "invalid sizes");
+  if (need > (size_t)MSIGN_NOALLOC_SCRATCH_BYTES)
+    return fail(MSIGN_ERR_WORKSPACE, "problem needs " + std::to_string(need) +
+                                         " bytes of scratch; msign_ns_noalloc holds " +
+                                         std::to_string((size_t)MSIGN_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  msign_status_t st = device_scratch(&ws);
+  if (st != MSIGN_OK) return st;
+  g_untimed = true;
+  st = ns_run(&g, 1, io_dtype, compute_dtype, steps, coeffs, eps, 0u, ws, need, stream);
+  g_untimed = false;
+  return st;
 }
 
 msign_status_t msign_ns_ex(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,

@@ -128,6 +128,19 @@ def test_ns_ex_rejects_unknown_flags():
     assert lib.syrk_xxt_ex(FAKE, FAKE2, 1, 8, 64, 1, 1.0, None, 0.0, 0.0, 2, None, 0, None) == 1
 
 
+def test_noalloc_rejects_before_touching_the_device():
+    """msign_ns_noalloc: sizes beyond its fixed scratch, bad dtypes and empty
+    problems are settled on the host (no device lookup, no launch)."""
+    lib = _lib()
+    assert lib.msign_ns_workspace_bytes(1, 1024, 4096, 1) <= mod.NOALLOC_SCRATCH_BYTES
+    assert lib.msign_ns_workspace_bytes(1, 2048, 4096, 1) > mod.NOALLOC_SCRATCH_BYTES
+    assert lib.msign_ns_noalloc(FAKE, FAKE, 1, 2048, 4096, 1, 1, 5, None, 1e-20, None) == 4
+    assert b"scratch" in lib.msign_last_error()
+    assert lib.msign_ns_noalloc(FAKE, FAKE, 1, 8, 16, 1, 9, 5, None, 1e-20, None) == 2
+    assert lib.msign_ns_noalloc(FAKE, FAKE, 1, 8, 16, 1, 1, 0, None, 1e-20, None) == 1
+    assert lib.msign_ns_noalloc(None, None, 0, 8, 16, 1, 1, 5, None, 1e-20, None) == 0
+
+
 def _gram(lib, restarts, n_restarts, steps=5, **kw):
     arr = (ctypes.c_int32 * len(restarts))(*restarts) if restarts is not None else None
     return lib.msign_gram_ns(FAKE, FAKE, 1, 8, 16, 1, 2, steps, None, 1e-20, arr, n_restarts,
