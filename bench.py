@@ -98,9 +98,10 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
     one matrix: the sum of squares reads the input; the normalise pass reads
     it again and writes the fp32 master (NS only) and the compute-dtype copy,
     padded to 64 (rows and columns).  The improved initial normalisation adds
-    its combine pass (reads A and A A, writes B); a Muon step adds the
-    momentum pass (reads M fp32 and G, writes M) and the update (reads W and
-    the fp32 direction, writes W), and its msign input is the fp32 M."""
+    its combine pass (reads A and A A, writes B).  In a Muon step the msign
+    input is the fp32 M and the sum-of-squares pass also reads G and writes
+    the updated M; the parameter update happens in the last product's
+    epilogue (not counted here)."""
     pad = lambda v: (v + 63) // 64 * 64
     n, m = min(rows, cols), max(rows, cols)
     elems, padded = rows * cols, pad(n) * pad(m)
@@ -109,7 +110,7 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
     if method == "ns_init":
         b += 3 * pad(n) * pad(n) * c_bytes
     if method == "muon_ns":
-        b += elems * (4 + io_bytes + 4) + elems * (io_bytes + 4 + io_bytes)
+        b += elems * (io_bytes + 4)
     return float(b)
 
 
@@ -118,7 +119,7 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
 # traffic figure is reported only while the kernel sources hash to the value
 # recorded with it; after any change to them it is stale and `traffic` is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_rect_8192x8192_bf16_traffic.md")
-KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "init_scale.hpp", "launch.hpp", "launch_impl.hpp", "muon.hpp",
+KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "init_scale.hpp", "launch.hpp", "launch_impl.hpp", "normalize.hpp",
                   "msign_api.hip", "products_dense.hip", "products_grouped.hip", "products_single.hip")
 
 

@@ -267,8 +267,11 @@ msign_status_t msign_gram_ns_grouped(const msign_group_t* groups, int32_t ngroup
  *     M <- mu M + G;   W <- W - lr msign(M)
  * with msign by standard NS (MUON_NS, as msign_ns_grouped with `flags`) or
  * Gram NS (MUON_GRAM, as msign_gram_ns_grouped; flags must be 0), all groups'
- * products in grouped launches.  M is fp32; msign(M) is formed in fp32 in the
- * workspace and W is rounded once, to io_dtype.
+ * products in grouped launches.  The step is fused into the msign call: the
+ * sum-of-squares pass that starts msign updates M in place (fp32, fmaf(mu,
+ * M, G)) and the epilogue of the last product updates W in place (msign(M)
+ * in fp32, W rounded once to io_dtype); there is no other pass and no buffer
+ * for msign(M), so the workspace is that of the msign call alone.
  *
  * Group g: w (parameters, updated in place) and g (gradient), device
  * [batch, rows, cols] in io_dtype; m (momentum, updated in place), device

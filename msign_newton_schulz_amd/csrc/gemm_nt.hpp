@@ -51,6 +51,8 @@ struct OutSpec {
   float diag;          // added where i == j and i < diag_lim
   int32_t diag_lim;
   int32_t vec_ok;      // 4 consecutive transposed elements may be one store
+  int32_t update;      // 0: store the value v; 1: update in place, out <- out + axpy v
+  float axpy;
 };
 
 struct GemmParams {
@@ -115,8 +117,33 @@ template <> struct Mma<float> {
   }
 };
 
+// Element idx of output os gets v, or (an update output) out + axpy v in
+// fp32, rounded once to the output's dtype.  UPD: the kernel may have
+// update outputs (rectangular products only: the last product of a fused
+// Muon step); triangle kernels compile without the branch.
+template <bool UPD>
+__device__ __forceinline__ void out_elem(const OutSpec& os, int64_t idx, float v) {
+  if (UPD && os.update) v = fmaf(os.axpy, v, load_as_f32(os.ptr, idx, os.dtype));
+  store_from_f32(os.ptr, idx, os.dtype, v);
+}
+
+// The same for four consecutive elements idx .. idx + 3 (one vector access).
+template <bool UPD>
+__device__ __forceinline__ void out_vec4(const OutSpec& os, int64_t idx, const float* w) {
+  if (UPD && os.update) {
+    float o[4];
+    load_vec4(os.ptr, idx, os.dtype, o);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = fmaf(os.axpy, w[r], o[r]);
+    store_vec4(os.ptr, idx, os.dtype, o);
+  } else {
+    store_vec4(os.ptr, idx, os.dtype, w);
+  }
+}
+
+template <bool UPD>
 __device__ __forceinline__ void store_elem(const OutSpec& os, int64_t bz, int64_t r, int64_t c, float v) {
-  store_from_f32(os.ptr, bz * os.bstride + r * os.ld + c, os.dtype, v);
+  out_elem<UPD>(os, bz * os.bstride + r * os.ld + c, v);
 }
 
 // 16-byte chunk position inside an LDS row of CPR chunks: XOR swizzle so
@@ -246,19 +273,19 @@ __device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r;
-        if (i < os.rows_lim && (!diag_tile || i <= j)) store_elem(os, bz, i, j, w[r]);
+        if (i < os.rows_lim && (!diag_tile || i <= j)) store_elem<!TRI>(os, bz, i, j, w[r]);
       }
     }
     if (TRI || os.transposed) {
       // element (i, j) goes to ptr[j * ld + i]; in triangle mode this is the mirror
       const int64_t base = bz * os.bstride + (int64_t)j * os.ld + i0;
       if (os.vec_ok && !diag_tile && i0 + 3 < os.rows_lim) {
-        store_vec4(os.ptr, base, os.dtype, w);
+        out_vec4<!TRI>(os, base, w);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
-          if (i < os.rows_lim && (!diag_tile || i < j)) store_from_f32(os.ptr, base + r, os.dtype, w[r]);
+          if (i < os.rows_lim && (!diag_tile || i < j)) out_elem<!TRI>(os, base + r, w[r]);
         }
       }
     }
@@ -429,7 +456,7 @@ __device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz,
       for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
         if (o >= p.nout) break;
         const OutSpec& os = p.out[o];
-        store_vec4(os.ptr, bz * os.bstride + (int64_t)j * os.ld + i, os.dtype, w);
+        out_vec4<true>(os, bz * os.bstride + (int64_t)j * os.ld + i, w);
       }
     }
   }

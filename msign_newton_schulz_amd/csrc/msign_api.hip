@@ -27,7 +27,6 @@
 #include "init_scale.hpp"
 #include "launch.hpp"
 #include "mfma_probe.hpp"
-#include "muon.hpp"
 #include "normalize.hpp"
 
 #include <atomic>
@@ -97,12 +96,25 @@ struct Carver {
   }
 };
 
-// One problem of a (grouped) call: batch matrices of rows x cols.
+// A Muon step fused around msign (see muon_run): the msign input x is the
+// fp32 momentum M, which the sum-of-squares pass updates in place to
+// fmaf(mu, M, G) before normalising it; the output y is the parameter W,
+// which the last product's epilogue updates in place, W <- W - lr msign(M).
+struct Fuse {
+  const void* g;
+  int32_t g_dtype;
+  float mu, lr;
+};
+
+// One problem of a (grouped) call: batch matrices of rows x cols; y in
+// y_dtype (the io dtype, except in a fused Muon step).
 struct Prob {
   const void* x;
   void* y;
   int64_t batch, rows, cols;
   Shape s;
+  int32_t y_dtype;
+  const Fuse* fuse;  // null: a plain msign
 };
 
 // Workspace regions of one problem of an NS call (offsets from the call's
@@ -449,7 +461,7 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
 
 // Shared checks of msign_ns / msign_gram_ns.
 msign_status_t check_common(const void* x, void* y, int64_t batch, int64_t rows, int64_t cols,
-                            int32_t io_dtype, int32_t compute_dtype, int32_t steps,
+                            int32_t io_dtype, int32_t y_dtype, int32_t compute_dtype, int32_t steps,
                             const float* coeffs, float eps, bool* empty) {
   *empty = false;
   if (!dt_valid(io_dtype)) return fail(MSIGN_ERR_DTYPE, "io_dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
@@ -471,18 +483,19 @@ msign_status_t check_common(const void* x, void* y, int64_t batch, int64_t rows,
   if ((double)batch * (double)s.np * (double)s.mp > 4.0e12)
     return fail(MSIGN_ERR_SHAPE, "problem too large");
   if (!x || !y) return fail(MSIGN_ERR_ARG, "x and y must be non-null");
-  if (!aligned(x, dt_size(io_dtype)) || !aligned(y, dt_size(io_dtype)))
+  if (!aligned(x, dt_size(io_dtype)) || !aligned(y, dt_size(y_dtype)))
     return fail(MSIGN_ERR_ARG, "x and y must be aligned to their element size");
   return MSIGN_OK;
 }
 
-msign_status_t check_ws_alias(const void* x, void* y, size_t io_bytes, void* ws, size_t ws_bytes, size_t need) {
+msign_status_t check_ws_alias(const void* x, size_t x_bytes, void* y, size_t y_bytes, void* ws, size_t ws_bytes,
+                              size_t need) {
   if (!ws || ws_bytes < need)
     return fail(MSIGN_ERR_WORKSPACE, "workspace is null or smaller than the required " + std::to_string(need) + " bytes");
   if (!aligned(ws, 256)) return fail(MSIGN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (overlap(y, io_bytes, ws, need) || overlap(x, io_bytes, ws, need))
+  if (overlap(y, y_bytes, ws, need) || overlap(x, x_bytes, ws, need))
     return fail(MSIGN_ERR_ALIAS, "x or y overlaps the workspace");
-  if (x != y && overlap(x, io_bytes, y, io_bytes))
+  if (x != y && overlap(x, x_bytes, y, y_bytes))
     return fail(MSIGN_ERR_ALIAS, "y partially overlaps x (only y == x is allowed)");
   return MSIGN_OK;
 }
@@ -491,11 +504,15 @@ msign_status_t check_ws_alias(const void* x, void* y, size_t io_bytes, void* ws,
 // (the wide orientation); converted here to the input's orientation.
 msign_status_t launch_normalize(const void* x, int32_t io_dtype, int64_t batch, int64_t rows, int64_t cols,
                                 const Shape& s, float* partial, int32_t nblk, float eps,
-                                const NormOut* outs_x, int nout, hipStream_t st) {
+                                const NormOut* outs_x, int nout, hipStream_t st, const Fuse* fuse = nullptr) {
   {
     TimedLaunch tl(KC_NORM, st);
     dim3 g1((unsigned)nblk, (unsigned)batch);
-    sumsq_partial_kernel<256><<<g1, 256, 0, st>>>(x, io_dtype, rows * cols, nblk, partial);
+    if (fuse)  // x is the fp32 momentum: M <- mu M + G first (Muon step)
+      sumsq_partial_kernel<256, true>
+          <<<g1, 256, 0, st>>>(x, io_dtype, rows * cols, nblk, partial, fuse->g, fuse->g_dtype, fuse->mu);
+    else
+      sumsq_partial_kernel<256><<<g1, 256, 0, st>>>(x, io_dtype, rows * cols, nblk, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "sumsq_partial_kernel");
   }
@@ -543,10 +560,16 @@ void coeff_at(const float* coeffs, int t, float* a, float* b, float* c) {
 // Final output y (io dtype, user layout) of a product C' = X^T Z (m x n, C'
 // [i][j] = X'[j][i]): wide -> y[j][i] (y is n x m, a transposed store),
 // tall -> y[i][j] (y is m x n).
-void add_final_out(GemmParams& g, void* y, const Shape& s, int32_t io_dtype) {
+// A fused Muon step updates y (the parameters) in place: y <- y - lr C.
+void add_final_out(GemmParams& g, const Prob& pr) {
+  const Shape& s = pr.s;
   const int64_t ld = s.tall ? s.n : s.m;
-  const bool vec = !s.tall && (s.m % 4 == 0) && aligned(y, 4 * dt_size(io_dtype));
-  add_out(g, y, ld, s.n * s.m, io_dtype, !s.tall, s.m, s.n, 0.f, 0, vec);
+  const bool vec = !s.tall && (s.m % 4 == 0) && aligned(pr.y, 4 * dt_size(pr.y_dtype));
+  add_out(g, pr.y, ld, s.n * s.m, pr.y_dtype, !s.tall, s.m, s.n, 0.f, 0, vec);
+  if (pr.fuse) {
+    g.out[g.nout - 1].update = 1;
+    g.out[g.nout - 1].axpy = -pr.fuse->lr;
+  }
 }
 
 }  // namespace
@@ -555,20 +578,25 @@ namespace {
 
 // Non-empty problems of a call, checked one by one; `*ng` of them.
 msign_status_t gather(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t cdt,
-                      int32_t steps, const float* coeffs, float eps, Prob* pr, int* ng) {
+                      int32_t steps, const float* coeffs, float eps, Prob* pr, int* ng, int32_t y_dtype = -1,
+                      const Fuse* fuse = nullptr) {
   *ng = 0;
+  if (y_dtype < 0) y_dtype = io_dtype;
   if (ngroups < 1 || ngroups > MSIGN_MAX_GROUPS)
     return fail(MSIGN_ERR_ARG, "ngroups must be in 1.." + std::to_string(MSIGN_MAX_GROUPS));
   if (!groups) return fail(MSIGN_ERR_ARG, "groups must be non-null");
   for (int i = 0; i < ngroups; ++i) {
     const msign_group_t& g = groups[i];
     bool empty = false;
-    msign_status_t st = check_common(g.x, g.y, g.batch, g.rows, g.cols, io_dtype, cdt, steps, coeffs, eps, &empty);
+    msign_status_t st =
+        check_common(g.x, g.y, g.batch, g.rows, g.cols, io_dtype, y_dtype, cdt, steps, coeffs, eps, &empty);
     if (st != MSIGN_OK) return ngroups > 1 ? fail(st, "group " + std::to_string(i) + ": " + g_err) : st;
     if (empty) continue;
     Prob& p = pr[(*ng)++];
     p.x = g.x; p.y = g.y; p.batch = g.batch; p.rows = g.rows; p.cols = g.cols;
     p.s = canon(g.rows, g.cols);
+    p.y_dtype = y_dtype;
+    p.fuse = fuse ? &fuse[i] : nullptr;
   }
   return MSIGN_OK;
 }
@@ -577,15 +605,15 @@ msign_status_t gather(const msign_group_t* groups, int32_t ngroups, int32_t io_d
 // apart within a problem, and no problem's output overlapping another
 // problem's input or output.
 msign_status_t check_call_ws(const Prob* pr, int ng, int32_t io_dtype, void* ws, size_t ws_bytes, size_t need) {
-  const size_t es = dt_size(io_dtype);
+  auto bytes = [&](const Prob& p, int32_t dt) { return (size_t)p.batch * p.rows * p.cols * dt_size(dt); };
   for (int i = 0; i < ng; ++i) {
-    const size_t bi = (size_t)pr[i].batch * pr[i].rows * pr[i].cols * es;
-    msign_status_t st = check_ws_alias(pr[i].x, pr[i].y, bi, ws, ws_bytes, need);
+    const size_t xi = bytes(pr[i], io_dtype), yi = bytes(pr[i], pr[i].y_dtype);
+    msign_status_t st = check_ws_alias(pr[i].x, xi, pr[i].y, yi, ws, ws_bytes, need);
     if (st != MSIGN_OK) return st;
     for (int j = 0; j < ng; ++j) {
       if (j == i) continue;
-      const size_t bj = (size_t)pr[j].batch * pr[j].rows * pr[j].cols * es;
-      if (overlap(pr[i].y, bi, pr[j].x, bj) || overlap(pr[i].y, bi, pr[j].y, bj))
+      if (overlap(pr[i].y, yi, pr[j].x, bytes(pr[j], io_dtype)) ||
+          overlap(pr[i].y, yi, pr[j].y, bytes(pr[j], pr[j].y_dtype)))
         return fail(MSIGN_ERR_ALIAS, "the output of one group overlaps the input or output of another");
     }
   }
@@ -689,7 +717,7 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
         {v.x32[0], v.s.mp, v.nm, MSIGN_F32, 0},
     };
     st = launch_normalize(pr[i].x, io_dtype, pr[i].batch, pr[i].rows, pr[i].cols, v.s, v.partial, pl.nblk, eps,
-                          outs, 2, stream);
+                          outs, 2, stream, pr[i].fuse);
     if (st != MSIGN_OK) return st;
   }
 
@@ -771,7 +799,7 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
           add_out(g, v.x32[nxt], v.s.mp, v.nm, MSIGN_F32, true, v.s.mp, v.s.np, 0.f, 0, true);
           add_out(g, v.xh[nxt], v.s.mp, v.nm, cdt, true, v.s.mp, v.s.np, 0.f, 0, true);
         } else {
-          add_final_out(g, pr[i].y, v.s, io_dtype);
+          add_final_out(g, pr[i]);
         }
       }
       TimedLaunch tl(KC_RECT, stream);
@@ -787,7 +815,8 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
 // are checked; each sub-call (see split_call) runs with its own dtype.
 msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
                       int32_t steps, const float* coeffs, float eps, uint32_t flags, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      size_t workspace_bytes, hipStream_t stream, int32_t y_dtype = -1,
+                      const Fuse* fuse = nullptr) {
   g_err.clear();
   if (flags & ~(uint32_t)(MSIGN_NS_IMPROVED_INIT | MSIGN_NS_DENSE_PRODUCTS)) return fail(MSIGN_ERR_ARG, "unknown flag");
   const bool improved = (flags & MSIGN_NS_IMPROVED_INIT) != 0;
@@ -796,7 +825,7 @@ msign_status_t ns_run(const msign_group_t* groups, int32_t ngroups, int32_t io_d
     return fail(MSIGN_ERR_ARG, "MSIGN_NS_DENSE_PRODUCTS does not combine with MSIGN_NS_IMPROVED_INIT");
   Prob pr[MSIGN_MAX_GROUPS];
   int ng = 0;
-  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng, y_dtype, fuse);
   if (st != MSIGN_OK || ng == 0) return st;
   if (dense && ng > 1) return fail(MSIGN_ERR_ARG, "MSIGN_NS_DENSE_PRODUCTS takes one non-empty group");
   const SubCalls sc = split_call<NsPlan>(pr, ng, compute_dtype, plan_ns_regions);
@@ -860,7 +889,8 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
     batches[i] = pr[i].batch;
     NormOut outs[1] = {{v.xh[0], v.s.mp, v.nm, cdt, 0}};
     st = launch_normalize(pr[i].x, io_dtype, pr[i].batch, pr[i].rows, pr[i].cols, v.s,
-                          reinterpret_cast<float*>(at(workspace, pl.partial)), pl.nblk, eps, outs, 1, stream);
+                          reinterpret_cast<float*>(at(workspace, pl.partial)), pl.nblk, eps, outs, 1, stream,
+                          pr[i].fuse);
     if (st != MSIGN_OK) return st;
   }
 
@@ -899,7 +929,7 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
     for (int i = 0; i < ng; ++i) {
       G& v = gv[i];
       qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, qc ? v.Qb1 : v.Qb0, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np, 1.f);
-      if (final_out) add_final_out(qs[i], pr[i].y, v.s, io_dtype);
+      if (final_out) add_final_out(qs[i], pr[i]);
       else add_out(qs[i], v.xh[cur ^ 1], v.s.mp, v.nm, cdt, true, v.s.mp, v.s.np, 0.f, 0, true);
     }
     TimedLaunch tl(KC_RECT, stream);
@@ -946,14 +976,15 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
 // checked here, each sub-call (see split_call) run with its own dtype.
 msign_status_t gram_run(const msign_group_t* groups, int32_t ngroups, int32_t io_dtype, int32_t compute_dtype,
                         int32_t steps, const float* coeffs, float eps, const int32_t* restart_after,
-                        int32_t n_restarts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        int32_t n_restarts, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        int32_t y_dtype = -1, const Fuse* fuse = nullptr) {
   g_err.clear();
   bool restart_at[MSIGN_MAX_STEPS + 1] = {false};
   msign_status_t st0 = parse_restarts(steps, restart_after, n_restarts, restart_at);
   if (st0 != MSIGN_OK) return st0;
   Prob pr[MSIGN_MAX_GROUPS];
   int ng = 0;
-  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng);
+  msign_status_t st = gather(groups, ngroups, io_dtype, compute_dtype, steps, coeffs, eps, pr, &ng, y_dtype, fuse);
   if (st != MSIGN_OK || ng == 0) return st;
   const SubCalls sc = split_call<GramPlan>(pr, ng, compute_dtype, plan_gram_regions);
   st = check_call_ws(pr, ng, io_dtype, workspace, workspace_bytes, sc.total);
@@ -969,14 +1000,13 @@ msign_status_t gram_run(const msign_group_t* groups, int32_t ngroups, int32_t io
 
 // ------------------------------------------------------------ Muon step --
 
-// msign groups of a Muon step: x = the momentum (fp32), y = the fp32
-// update direction in the step's workspace (at offsets o_off[i]).
+// msign groups of a Muon step: x = the fp32 momentum M, y = the parameters
+// W; the step itself is fused into the msign call (see Fuse).
 struct MuonCall {
   int ng;
   msign_group_t mg[MSIGN_MAX_GROUPS];
   const muon_group_t* src[MSIGN_MAX_GROUPS];
-  size_t o_off[MSIGN_MAX_GROUPS];
-  size_t msign_off, total;
+  size_t total;
 };
 
 bool muon_shape_ok(const muon_group_t& g) {
@@ -984,9 +1014,8 @@ bool muon_shape_ok(const muon_group_t& g) {
          g.batch <= kMaxBatch;
 }
 
-// Plans the workspace; the msign groups' pointers are those of `ws` (null
-// for a size query).
-msign_status_t plan_muon(const muon_group_t* groups, int32_t ngroups, int32_t method, int32_t cdt, void* ws,
+// Non-empty groups and the workspace size (that of the msign call).
+msign_status_t plan_muon(const muon_group_t* groups, int32_t ngroups, int32_t method, int32_t cdt,
                          MuonCall* mc) {
   mc->ng = 0;
   if (ngroups < 1 || ngroups > MSIGN_MAX_GROUPS)
@@ -994,36 +1023,28 @@ msign_status_t plan_muon(const muon_group_t* groups, int32_t ngroups, int32_t me
   if (!groups) return fail(MSIGN_ERR_ARG, "groups must be non-null");
   if (method != MUON_NS && method != MUON_GRAM) return fail(MSIGN_ERR_ARG, "method must be MUON_NS or MUON_GRAM");
   if (!dt_valid(cdt)) return fail(MSIGN_ERR_DTYPE, "compute_dtype must be MSIGN_F32, MSIGN_BF16 or MSIGN_F16");
-  Carver c;
   for (int i = 0; i < ngroups; ++i) {
     const muon_group_t& g = groups[i];
     if (!muon_shape_ok(g)) return fail(MSIGN_ERR_SHAPE, "group " + std::to_string(i) + ": invalid shape");
     if (g.batch == 0 || g.rows == 0 || g.cols == 0) continue;
     const int k = mc->ng++;
     mc->src[k] = &g;
-    mc->o_off[k] = c.take((size_t)g.batch * g.rows * g.cols * 4);
-  }
-  mc->msign_off = c.off;
-  for (int k = 0; k < mc->ng; ++k) {
-    const muon_group_t& g = *mc->src[k];
     mc->mg[k].x = g.m;
-    mc->mg[k].y = ws ? at(ws, mc->o_off[k]) : nullptr;
+    mc->mg[k].y = g.w;
     mc->mg[k].batch = g.batch;
     mc->mg[k].rows = g.rows;
     mc->mg[k].cols = g.cols;
   }
   const size_t need = mc->ng == 0 ? 0 : call_workspace(mc->mg, mc->ng, cdt, method == MUON_GRAM);
   if (need == (size_t)-1) return fail(MSIGN_ERR_SHAPE, "invalid sizes");
-  mc->total = mc->ng == 0 ? 0 : mc->msign_off + need;
+  mc->total = need;
   return MSIGN_OK;
 }
 
-unsigned elementwise_blocks(int64_t n) {
-  int64_t b = (n + 1023) / 1024;
-  if (b > 4096) b = 4096;
-  return (unsigned)(b < 1 ? 1 : b);
-}
-
+// One Muon step as one msign call: the sum-of-squares pass first forms
+// M <- mu M + G in place (fp32), and the last product's epilogue writes
+// W <- W - lr msign(M) in place (fp32 arithmetic, W rounded once).  No
+// other pass and no buffer for msign(M).
 msign_status_t muon_run(const muon_group_t* groups, int32_t ngroups, int32_t io_dtype, float mu, float lr,
                         int32_t method, int32_t compute_dtype, int32_t steps, const float* coeffs, float eps,
                         uint32_t flags, const int32_t* restart_after, int32_t n_restarts, void* workspace,
@@ -1039,7 +1060,7 @@ msign_status_t muon_run(const muon_group_t* groups, int32_t ngroups, int32_t io_
     if (st0 != MSIGN_OK) return st0;
   }
   MuonCall mc;
-  msign_status_t st = plan_muon(groups, ngroups, method, compute_dtype, workspace, &mc);
+  msign_status_t st = plan_muon(groups, ngroups, method, compute_dtype, &mc);
   if (st != MSIGN_OK || mc.ng == 0) return st;
   if (!workspace || workspace_bytes < mc.total)
     return fail(MSIGN_ERR_WORKSPACE, "workspace is null or smaller than the required " + std::to_string(mc.total) + " bytes");
@@ -1050,12 +1071,6 @@ msign_status_t muon_run(const muon_group_t* groups, int32_t ngroups, int32_t io_
     if (!g.w || !g.g || !g.m) return fail(MSIGN_ERR_ARG, "w, g and m must be non-null");
     if (!aligned(g.w, es) || !aligned(g.g, es) || !aligned(g.m, 4))
       return fail(MSIGN_ERR_ARG, "w, g and m must be aligned to their element size");
-  }
-  {  // the msign call's own checks, before anything is launched
-    Prob pr[MSIGN_MAX_GROUPS];
-    int ng = 0;
-    st = gather(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, pr, &ng);
-    if (st != MSIGN_OK) return st;
   }
   // buffers: w and m written, g read; none may overlap the workspace, and a
   // written buffer may overlap no other buffer
@@ -1076,36 +1091,15 @@ msign_status_t muon_run(const muon_group_t* groups, int32_t ngroups, int32_t io_
       if (j != i && (bufs[i].written || bufs[j].written) && overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
         return fail(MSIGN_ERR_ALIAS, "w or m overlaps another buffer of the step");
   }
-  // M <- mu M + G
-  for (int k = 0; k < mc.ng; ++k) {
-    const muon_group_t& g = *mc.src[k];
-    const int64_t n = g.batch * g.rows * g.cols;
-    const int32_t vec = aligned(g.m, 16) && aligned(g.g, 4 * es) ? 1 : 0;
-    TimedLaunch tl(KC_NORM, stream);
-    momentum_kernel<<<elementwise_blocks(n), 256, 0, stream>>>(g.m, g.g, io_dtype, n, mu, vec);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "momentum_kernel");
-  }
-  // O = msign(M), fp32, into the workspace
-  void* ms_ws = at(workspace, mc.msign_off);
-  const size_t ms_bytes = workspace_bytes - mc.msign_off;
-  st = method == MUON_NS
-           ? ns_run(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, flags, ms_ws, ms_bytes, stream)
-           : gram_run(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, restart_after, n_restarts, ms_ws,
-                      ms_bytes, stream);
-  if (st != MSIGN_OK) return st;
-  // W <- W - lr O
-  for (int k = 0; k < mc.ng; ++k) {
-    const muon_group_t& g = *mc.src[k];
-    const int64_t n = g.batch * g.rows * g.cols;
-    const float* o = reinterpret_cast<const float*>(at(workspace, mc.o_off[k]));
-    const int32_t vec = aligned(g.w, 4 * es) ? 1 : 0;
-    TimedLaunch tl(KC_NORM, stream);
-    update_kernel<<<elementwise_blocks(n), 256, 0, stream>>>(g.w, io_dtype, o, n, lr, vec);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "update_kernel");
-  }
-  return MSIGN_OK;
+  Fuse fz[MSIGN_MAX_GROUPS];
+  for (int k = 0; k < mc.ng; ++k) fz[k] = Fuse{mc.src[k]->g, io_dtype, mu, lr};
+  // msign of the fp32 momentum into the io-dtype parameters, step fused;
+  // its own checks all run before its first launch
+  return method == MUON_NS
+             ? ns_run(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, flags, workspace,
+                      workspace_bytes, stream, io_dtype, fz)
+             : gram_run(mc.mg, mc.ng, MSIGN_F32, compute_dtype, steps, coeffs, eps, restart_after, n_restarts,
+                        workspace, workspace_bytes, stream, io_dtype, fz);
 }
 
 // ------------------------------------------------- allocation-free calls --
@@ -1232,7 +1226,7 @@ size_t muon_step_workspace_bytes(const muon_group_t* groups, int32_t ngroups, in
                                  int32_t compute_dtype) {
   MuonCall mc;
   const std::string keep = g_err;
-  const msign_status_t st = plan_muon(groups, ngroups, method, compute_dtype, nullptr, &mc);
+  const msign_status_t st = plan_muon(groups, ngroups, method, compute_dtype, &mc);
   g_err = keep;
   return st == MSIGN_OK ? mc.total : (size_t)-1;
 }

@@ -40,9 +40,14 @@ struct NormParams {
   int32_t nout;
 };
 
-template <int NT>
+// MOM (a Muon step's momentum, folded into this pass): x is the fp32
+// momentum M, updated in place to fmaf(mu, M, G) (G of dtype gdt, the same
+// layout), and the sum is taken over the updated values.  Every element is
+// read and written by one thread only.
+template <int NT, bool MOM = false>
 __global__ void __launch_bounds__(NT)
-sumsq_partial_kernel(const void* x, int32_t dt, int64_t count, int32_t nblk, float* partial) {
+sumsq_partial_kernel(const void* x, int32_t dt, int64_t count, int32_t nblk, float* partial,
+                     const void* g = nullptr, int32_t gdt = DT_F32, float mu = 0.f) {
   const int64_t b = blockIdx.y;
   const int tid = threadIdx.x;
   const int esz = dt == DT_F32 ? 4 : 2;
@@ -52,7 +57,35 @@ sumsq_partial_kernel(const void* x, int32_t dt, int64_t count, int32_t nblk, flo
   const int64_t end = start + chunk < count ? start + chunk : count;
 
   float s = 0.f;
-  if (start < end) {
+  if constexpr (MOM) {
+    float* m = reinterpret_cast<float*>(const_cast<char*>(base));
+    const char* gb = static_cast<const char*>(g) + b * count * (gdt == DT_F32 ? 4 : 2);
+    if (start < end) {
+      const bool aligned = ((reinterpret_cast<uintptr_t>(m) | reinterpret_cast<uintptr_t>(gb)) & 15) == 0;
+      int64_t done = start;
+      if (aligned) {
+        const int64_t nvec = (end - start) / 4;
+        for (int64_t v = tid; v < nvec; v += NT) {
+          const int64_t e = start + v * 4;
+          float gv[4];
+          load_vec4(gb, e, gdt, gv);
+          f32x4 mv = *reinterpret_cast<const f32x4*>(m + e);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            mv[q] = fmaf(mu, mv[q], gv[q]);
+            s += mv[q] * mv[q];
+          }
+          *reinterpret_cast<f32x4*>(m + e) = mv;
+        }
+        done = start + nvec * 4;
+      }
+      for (int64_t e = done + tid; e < end; e += NT) {
+        const float f = fmaf(mu, m[e], load_as_f32(gb, e, gdt));
+        m[e] = f;
+        s += f * f;
+      }
+    }
+  } else if (start < end) {
     const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15) == 0;
     int64_t done = start;
     if (aligned) {
