@@ -95,7 +95,9 @@ def class_flops(n, m):
 
 def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
     """Algorithmic HBM bytes of the class-0 (HBM-bound) passes of one msign on
-    one matrix: the sum of squares reads the input; the normalise pass reads
+    one matrix: the sum of squares reads the input.  A wide input already in
+    the compute dtype with cols a multiple of 64 is then read by the first
+    products themselves (no other pass).  Otherwise the normalise pass reads
     it again and writes the fp32 master (NS only) and the compute-dtype copy,
     padded to 64 (rows and columns).  The improved initial normalisation adds
     its combine pass (reads A and A A, writes B).  In a Muon step the msign
@@ -106,6 +108,8 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
     n, m = min(rows, cols), max(rows, cols)
     elems, padded = rows * cols, pad(n) * pad(m)
     x_bytes = 4 if method == "muon_ns" else io_bytes
+    if method in ("ns", "gram") and rows <= cols and cols % 64 == 0 and io_bytes == c_bytes:
+        return float(elems * x_bytes)
     b = 2 * elems * x_bytes + padded * (c_bytes + (0 if method == "gram" else 4))
     if method == "ns_init":
         b += 3 * pad(n) * pad(n) * c_bytes

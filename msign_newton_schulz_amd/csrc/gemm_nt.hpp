@@ -73,6 +73,9 @@ struct GemmParams {
   // Optional per-matrix factor computed on the device: every value
   // (alpha acc + beta D) is multiplied by vscale[4 bz].
   const float* vscale;
+  // K-major P (AT) only: rows of P that exist (0: all K); rows from kvalid
+  // up to K read as zeros.
+  int32_t kvalid;
   // Optional, triangle products: sums of acc^2 over each tile (off-diagonal
   // tiles counted twice, for their mirror), one per (tile, wave, fragment
   // row) at sumsq[((bz tpm + tile) WG + wave) FM + fm]; the slots of the
@@ -669,7 +672,7 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
   // matrix's last row return zeros; columns past M feed only rows of the
   // result that are never stored.
   const char* Pk = static_cast<const char*>(p.P) + (bz * p.sp + m0) * ESZ;
-  const int64_t pk_bytes = ((int64_t)p.K * p.ldp - m0) * ESZ;
+  const int64_t pk_bytes = ((int64_t)(p.kvalid > 0 ? p.kvalid : p.K) * p.ldp - m0) * ESZ;
   // Chunk s sits NT / CPRA K rows below chunk 0 (with K-split waves, the
   // same row of slice s); when that is a multiple of the swizzle's period in
   // k (16) its LDS slot is chunk 0's plus s NT.
@@ -734,6 +737,36 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
   // 128 x 128 wave tile holds its A fragments and streams B fragments one at
   // a time to stay within the register file next to 256 accumulators.
   constexpr bool kAllFrags = (FM + FN) <= 12;
+  // Triangle products with direct loads and two MFMA sub-steps per slice
+  // put the barrier between the sub-steps (measured on the 256 x 256 tier:
+  // X X^T and A A 2.5-7 % faster, bit-identical; the rectangular product with
+  // its transpose reads gained nothing, and 14 % less in the unrolled form).
+  constexpr bool DEFER = !AT && NST == 0 && KSUB == 2 && kAllFrags && KW == 1;
+  // A and B fragments of MFMA sub-step kk of the K slice in `stage`
+  // (row-major operands, all-fragments wave tiles; the deferred loop below)
+  auto read_frags = [&](const u32x4* stage, const int kk, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+    const int ch = kk * 4 + (lane >> 4);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int row = wm * WM + fm * 16 + (lane & 15);
+      a[fm] = stage[row * CPR + swz<CPR>(row, ch)];
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int row = wn * WN + fn * 16 + (lane & 15);
+      b[fn] = stage[(BM + row) * CPR + swz<CPR>(row, ch)];
+    }
+  };
+  // the sub-step's products, B fragment by B fragment (each B fragment is
+  // dead after its FM products, so its register can take the next read)
+  auto mma_frags = [&](const u32x4 (&a)[FM], const u32x4 (&b)[FN]) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) Mma<T>::run(acc[fm][fn], a[fm], b[fn]);
+    __builtin_amdgcn_s_setprio(0);
+  };
   auto compute = [&](const u32x4* stage) {
     __builtin_amdgcn_s_setprio(1);  // favour waves that are issuing MFMAs
 #pragma unroll
@@ -849,6 +882,40 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
                                                  0, 0, 0);
       }
     };
+    if constexpr (DEFER) {
+      // The barrier sits between a slice's two MFMA sub-steps.  Iteration j
+      // (slice j in stage j & 1, its sub-step-0 fragments already in
+      // registers): sub-step 0's products; sub-step 1's reads; wait for this
+      // wave's loads of slice j + 1 and its reads, barrier (slice j + 1 is
+      // then whole and stage j & 1 free); loads of slice j + 2 into stage
+      // j & 1; sub-step 1's products, whose fragments crossed the barrier in
+      // registers, so every wave has MFMAs to issue right after it while the
+      // reads of slice j + 1's sub-step 0 follow.  Two stages, one barrier
+      // per slice, as before.
+      static_assert(KSUB == 2 && kAllFrags && KW == 1, "deferred barrier layout");
+      u32x4 fa[FM], fb[FN];
+      // One iteration; `cur` holds slice j, `nxt` takes slice j + 1.
+      auto iter = [&](u32x4* cur, const u32x4* nxt, int j) {
+        mma_frags(fa, fb);
+        read_frags(cur, 1, fa, fb);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (j + 2 < nk) issue(cur, (kt0 + j + 2) * KTE);
+        mma_frags(fa, fb);
+        if (j + 1 < nk) read_frags(nxt, 0, fa, fb);
+      };
+      // Two iterations per trip with both stages as non-aliasing pointers,
+      // so that no read waits for the loads in flight into the other stage.
+      auto trip = [&](u32x4* __restrict__ s0, u32x4* __restrict__ s1, int j) {
+        iter(s0, s1, j);
+        if (j + 1 < nk) iter(s1, s0, j + 1);
+      };
+      if (nk > 0) issue(lds[0], kt0 * KTE);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (nk > 1) issue(lds[1], (kt0 + 1) * KTE);
+      if (nk > 0) read_frags(lds[0], 0, fa, fb);
+      for (int j = 0; j < nk; j += 2) trip(lds[0], lds[1], j);
+      // the last barrier came after every read of the ring: it is free
+    } else {
     // (one step: the loads into `wr` and the reads from `rd` are declared
     // not to alias, so the reads need not wait for the loads in flight)
     auto step = [&](const u32x4* __restrict__ rd, u32x4* __restrict__ wr, bool load_next, int k_next) {
@@ -860,6 +927,7 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
     for (int j = 0; j < nk; ++j) {
       step(lds[j & 1], lds[(j + 1) & 1], j + 1 < nk, (kt0 + j + 1) * KTE);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     }
   } else {
   // steps of KW slices; wave kw computes slice j * KW + kw of step j when

@@ -127,7 +127,7 @@ struct NsPlan {
 
 struct GramPlan {
   int32_t nblk;
-  size_t xh[2], r, z, rz, q[2], partial;
+  size_t xh[2], r, z, rz, q[2], partial, scales;
 };
 
 template <typename P>
@@ -163,6 +163,7 @@ void plan_gram_regions(const Prob& pr, int32_t cdt, Carver& c, GramPlan& p) {
   p.q[0] = c.take(nn * cs);
   p.q[1] = c.take(nn * cs);
   p.partial = c.take((size_t)pr.batch * p.nblk * 4);
+  p.scales = c.take((size_t)pr.batch * 4 * 4);
 }
 
 // Every problem's regions, one after the other, then the K-split scratch.
@@ -500,6 +501,33 @@ msign_status_t check_ws_alias(const void* x, size_t x_bytes, void* y, size_t y_b
   return MSIGN_OK;
 }
 
+// The first products may read the input itself instead of normalised
+// copies: a wide matrix (no transpose) already in the compute dtype, whose
+// rows are whole 64-element K slices (cols a multiple of 64) starting on 16
+// bytes.  The normalisation X0 = X / s then becomes per-matrix factors of
+// those products' epilogues: 1/s^2 for the first X X^T and 1/s for the first
+// product with X (the rectangular step, or Gram's Q X), applied in fp32 to
+// the accumulated values.  Not with a fused Muon step (its input is the fp32
+// momentum) or the improved initial normalisation (its own first-step factor).
+bool direct_input(const Prob& pr, int32_t io_dtype, int32_t cdt) {
+  return !pr.s.tall && io_dtype == cdt && pr.s.m % kPad == 0 && aligned(pr.x, 16) && pr.fuse == nullptr;
+}
+
+// Sum of squares, then the per-matrix factors of a direct first step into
+// nscale[4 b] (1/s^2) and nscale[4 b + 1] (1/s).
+msign_status_t launch_norm_scale(const void* x, int32_t io_dtype, int64_t batch, int64_t count, float* partial,
+                                 int32_t nblk, float eps, float* nscale, hipStream_t st) {
+  TimedLaunch tl(KC_NORM, st);
+  dim3 g1((unsigned)nblk, (unsigned)batch);
+  sumsq_partial_kernel<256><<<g1, 256, 0, st>>>(x, io_dtype, count, nblk, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "sumsq_partial_kernel");
+  norm_scale_kernel<<<dim3((unsigned)batch), 256, 0, st>>>(partial, nblk, eps, nscale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "norm_scale_kernel");
+  return MSIGN_OK;
+}
+
 // Sum of squares + scaled copies.  outs[k].transposed is relative to X
 // (the wide orientation); converted here to the input's orientation.
 msign_status_t launch_normalize(const void* x, int32_t io_dtype, int64_t batch, int64_t rows, int64_t cols,
@@ -692,6 +720,7 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
     int64_t nm, nn;
     void *x32[2], *xh[2], *A, *B;
     float *partial, *sumsq, *scales;
+    bool direct;  // the first products read the input (scales: 1/s^2, 1/s)
   } gv[MSIGN_MAX_GROUPS];
   int64_t batches[MSIGN_MAX_GROUPS];
   for (int i = 0; i < ng; ++i) {
@@ -710,6 +739,13 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
     v.sumsq = reinterpret_cast<float*>(at(workspace, pl.sumsq));
     v.scales = reinterpret_cast<float*>(at(workspace, pl.scales));
     batches[i] = pr[i].batch;
+    v.direct = !improved && direct_input(pr[i], io_dtype, cdt);
+    if (v.direct) {
+      st = launch_norm_scale(pr[i].x, io_dtype, pr[i].batch, pr[i].rows * pr[i].cols, v.partial, pl.nblk, eps,
+                             v.scales, stream);
+      if (st != MSIGN_OK) return st;
+      continue;
+    }
     // X0 (n x m): in the compute dtype (the X X^T operand, also read
     // K-major as X^T by the update) and the fp32 master
     NormOut outs[2] = {
@@ -730,7 +766,13 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
     {  // A = X X^T
       for (int i = 0; i < ng; ++i) {
         const G& v = gv[i];
-        qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
+        if (t == 0 && v.direct) {  // the input itself, n true rows, times 1/s^2
+          const int64_t nm = v.s.n * v.s.m;
+          qs[i] = gemm_base(pr[i].x, v.s.m, nm, pr[i].x, v.s.m, nm, v.s.n, v.s.n, v.s.mp, 1.f);
+          qs[i].vscale = v.scales;
+        } else {
+          qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
+        }
         add_out(qs[i], v.A, v.s.np, v.nn, cdt, dense, v.s.np, v.s.np, 0.f, 0, true);
       }
       TimedLaunch tl(KC_SYRK, stream);
@@ -791,10 +833,21 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
       for (int i = 0; i < ng; ++i) {
         const G& v = gv[i];
         GemmParams& g = qs[i];
-        g = gemm_base(v.xh[cur], v.s.mp, v.nm, cubic ? v.A : v.B, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np,
-                      cubic ? b : 1.f);
-        if (rescale) g.vscale = v.scales;
-        set_d(g, v.x32[cur], v.s.mp, v.nm, MSIGN_F32, a, true);
+        if (t == 0 && v.direct) {
+          // X = the input (n true rows, read K-major; D = the input in its
+          // own dtype), every value times 1/s
+          const int64_t nm = v.s.n * v.s.m;
+          g = gemm_base(pr[i].x, v.s.m, nm, cubic ? v.A : v.B, v.s.np, v.nn, v.s.mp, v.s.n, v.s.np,
+                        cubic ? b : 1.f);
+          g.kvalid = (int32_t)v.s.n;
+          g.vscale = v.scales + 1;
+          set_d(g, pr[i].x, v.s.m, nm, io_dtype, a, true);
+        } else {
+          g = gemm_base(v.xh[cur], v.s.mp, v.nm, cubic ? v.A : v.B, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np,
+                        cubic ? b : 1.f);
+          if (rescale) g.vscale = v.scales;
+          set_d(g, v.x32[cur], v.s.mp, v.nm, MSIGN_F32, a, true);
+        }
         if (t + 1 < steps) {
           add_out(g, v.x32[nxt], v.s.mp, v.nm, MSIGN_F32, true, v.s.mp, v.s.np, 0.f, 0, true);
           add_out(g, v.xh[nxt], v.s.mp, v.nm, cdt, true, v.s.mp, v.s.np, 0.f, 0, true);
@@ -871,6 +924,8 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
     Shape s;
     int64_t nm, nn;
     void *xh[2], *R, *Z, *RZ, *Qb0, *Qb1;  // Q double-buffered
+    float* scales;
+    bool direct;  // X0 is the input itself until the first restart (scales: 1/s^2, 1/s)
   } gv[MSIGN_MAX_GROUPS];
   int64_t batches[MSIGN_MAX_GROUPS];
   for (int i = 0; i < ng; ++i) {
@@ -887,20 +942,34 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
     v.Qb0 = at(workspace, pl.q[0]);
     v.Qb1 = at(workspace, pl.q[1]);
     batches[i] = pr[i].batch;
-    NormOut outs[1] = {{v.xh[0], v.s.mp, v.nm, cdt, 0}};
-    st = launch_normalize(pr[i].x, io_dtype, pr[i].batch, pr[i].rows, pr[i].cols, v.s,
-                          reinterpret_cast<float*>(at(workspace, pl.partial)), pl.nblk, eps, outs, 1, stream,
-                          pr[i].fuse);
+    v.scales = reinterpret_cast<float*>(at(workspace, pl.scales));
+    float* partial = reinterpret_cast<float*>(at(workspace, pl.partial));
+    v.direct = direct_input(pr[i], io_dtype, cdt);
+    if (v.direct) {
+      st = launch_norm_scale(pr[i].x, io_dtype, pr[i].batch, pr[i].rows * pr[i].cols, partial, pl.nblk, eps,
+                             v.scales, stream);
+    } else {
+      NormOut outs[1] = {{v.xh[0], v.s.mp, v.nm, cdt, 0}};
+      st = launch_normalize(pr[i].x, io_dtype, pr[i].batch, pr[i].rows, pr[i].cols, v.s, partial, pl.nblk, eps,
+                            outs, 1, stream, pr[i].fuse);
+    }
     if (st != MSIGN_OK) return st;
   }
 
   hipError_t e;
   int cur = 0, qc = 0;
+  bool raw = true;  // X is still X0 (the input itself for direct groups)
   GemmParams qs[MSIGN_MAX_GROUPS];
   auto gram_xxt = [&]() -> msign_status_t {
     for (int i = 0; i < ng; ++i) {
       const G& v = gv[i];
-      qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
+      if (raw && v.direct) {  // the input, n true rows, times 1/s^2
+        const int64_t nm = v.s.n * v.s.m;
+        qs[i] = gemm_base(pr[i].x, v.s.m, nm, pr[i].x, v.s.m, nm, v.s.n, v.s.n, v.s.mp, 1.f);
+        qs[i].vscale = v.scales;
+      } else {
+        qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
+      }
       add_out(qs[i], v.R, v.s.np, v.nn, cdt, false, v.s.np, v.s.np, 0.f, 0, true);
     }
     TimedLaunch tl(KC_SYRK, stream);
@@ -928,7 +997,14 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
   auto apply_q = [&](bool final_out, const char* what) -> msign_status_t {
     for (int i = 0; i < ng; ++i) {
       G& v = gv[i];
-      qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, qc ? v.Qb1 : v.Qb0, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np, 1.f);
+      if (raw && v.direct) {  // the input read K-major (n true rows), times 1/s
+        const int64_t nm = v.s.n * v.s.m;
+        qs[i] = gemm_base(pr[i].x, v.s.m, nm, qc ? v.Qb1 : v.Qb0, v.s.np, v.nn, v.s.mp, v.s.n, v.s.np, 1.f);
+        qs[i].kvalid = (int32_t)v.s.n;
+        qs[i].vscale = v.scales + 1;
+      } else {
+        qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, qc ? v.Qb1 : v.Qb0, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np, 1.f);
+      }
       if (final_out) add_final_out(qs[i], pr[i]);
       else add_out(qs[i], v.xh[cur ^ 1], v.s.mp, v.nm, cdt, true, v.s.mp, v.s.np, 0.f, 0, true);
     }
@@ -964,6 +1040,7 @@ msign_status_t gram_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, 
       st = apply_q(false, "restart X <- Q X");
       if (st != MSIGN_OK) return st;
       cur ^= 1;
+      raw = false;
       st = gram_xxt();
       if (st != MSIGN_OK) return st;
       fresh = true;

@@ -89,24 +89,49 @@ sumsq_partial_kernel(const void* x, int32_t dt, int64_t count, int32_t nblk, flo
     const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15) == 0;
     int64_t done = start;
     if (aligned) {
+      // 8 elements per 16-byte (or two, fp32) load; each thread keeps U
+      // loads in flight before summing them (in a fixed order)
+      constexpr int U = 4;
       const int64_t nvec = (end - start) / 8;
-      for (int64_t v = tid; v < nvec; v += NT) {
-        const int64_t e = start + v * 8;
+      auto sum8 = [&](const u32x4& u, const u32x4& w) {
+        float t = 0.f;
         if (dt == DT_F32) {
-          const f32x4* pv = reinterpret_cast<const f32x4*>(base + e * 4);
-          f32x4 u = pv[0], w = pv[1];
+          const f32x4 fu = __builtin_bit_cast(f32x4, u), fw = __builtin_bit_cast(f32x4, w);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) s += u[q] * u[q] + w[q] * w[q];
+          for (int q = 0; q < 4; ++q) t += fu[q] * fu[q] + fw[q] * fw[q];
         } else {
-          u32x4 u = *reinterpret_cast<const u32x4*>(base + e * 2);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint16_t lo = u[q] & 0xffff, hi = u[q] >> 16;
             const float f0 = dt == DT_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
             const float f1 = dt == DT_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
-            s += f0 * f0 + f1 * f1;
+            t += f0 * f0 + f1 * f1;
           }
         }
+        return t;
+      };
+      auto load8 = [&](int64_t v, u32x4& u, u32x4& w) {
+        const int64_t e = start + v * 8;
+        if (dt == DT_F32) {
+          const u32x4* pv = reinterpret_cast<const u32x4*>(base + e * 4);
+          u = pv[0];
+          w = pv[1];
+        } else {
+          u = *reinterpret_cast<const u32x4*>(base + e * 2);
+        }
+      };
+      int64_t v = tid;
+      for (; v + (U - 1) * NT < nvec; v += U * NT) {
+        u32x4 u[U], w[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) load8(v + k * NT, u[k], w[k]);
+#pragma unroll
+        for (int k = 0; k < U; ++k) s += sum8(u[k], w[k]);
+      }
+      for (; v < nvec; v += NT) {
+        u32x4 u, w;
+        load8(v, u, w);
+        s += sum8(u, w);
       }
       done = start + nvec * 8;
     }
@@ -125,6 +150,30 @@ sumsq_partial_kernel(const void* x, int32_t dt, int64_t count, int32_t nblk, flo
     float t = 0.f;
     for (int w = 0; w < NT / 64; ++w) t += ws[w];
     partial[b * nblk + blockIdx.x] = t;
+  }
+}
+
+// Per-matrix factors of a normalisation left to the products: one block
+// per matrix adds its partial sums in a fixed order and writes
+// out[4 b] = 1 / (sum + eps) and out[4 b + 1] = 1 / sqrt(sum + eps), the
+// factors of X X^T and of X in the first products of the iteration.
+__global__ void __launch_bounds__(256)
+norm_scale_kernel(const float* partial, int32_t nblk, float eps, float* out) {
+  __shared__ float wsum[4];
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x;
+  float s = 0.f;
+  for (int i = tid; i < nblk; i += 256) s += partial[b * nblk + i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = s;
+  __syncthreads();
+  if (tid == 0) {
+    const float r = 1.0f / sqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) + eps);
+    out[4 * b] = r * r;
+    out[4 * b + 1] = r;
+    out[4 * b + 2] = 0.f;
+    out[4 * b + 3] = 0.f;
   }
 }
 
