@@ -85,12 +85,14 @@ def mfma_loop_peak(M, dtype, launches=5, iters=20000):
     return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
-def class_flops(n, m):
+def class_flops(n, m, steps=5):
     """Algorithmic flops of one launch of each kernel class on one matrix
     ("Gram Newton-Schulz" §2.4 counts): a triangle product counts half of the
     dense work, so X X^T is m n^2, an n x n product n^3 and B X (or Q X)
-    2 m n^2."""
-    return {"xxt": float(m) * n * n, "square": float(n) ** 3, "rect": 2.0 * m * n * n}
+    2 m n^2.  The whole-iteration kernel of small matrices computes every
+    tile of its T steps: T (4 m n^2 + 2 n^3)."""
+    return {"xxt": float(m) * n * n, "square": float(n) ** 3, "rect": 2.0 * m * n * n,
+            "small": steps * (4.0 * m * n * n + 2.0 * n ** 3)}
 
 
 def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
@@ -124,6 +126,7 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
 # recorded with it; after any change to them it is stale and `traffic` is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_rect_8192x8192_bf16_traffic.md")
 KERNEL_SOURCES = ("common.hpp", "gemm_nt.hpp", "init_scale.hpp", "launch.hpp", "launch_impl.hpp", "normalize.hpp",
+                  "small_ns.hpp",
                   "msign_api.hip", "products_dense.hip", "products_grouped.hip", "products_single.hip")
 
 
@@ -303,7 +306,7 @@ def run_case(name, steps, warmup, with_cpu, with_timing, with_extras=False):
         M.kernel_timing(False)
         # roofline pass: the same K steps again, the dominant class's
         # launches bracketed by HIP events on the launch stream
-        dom = max(("xxt", "square", "rect"), key=lambda k: probe[k][0])
+        dom = max(("xxt", "square", "rect", "small"), key=lambda k: probe[k][0])
         M.kernel_timing(True, classes=[dom])
         torch.cuda.synchronize()
         p0 = time.perf_counter()
@@ -318,7 +321,7 @@ def run_case(name, steps, warmup, with_cpu, with_timing, with_extras=False):
     nmat = sum(x.shape[0] for x in xs)
     eff = 0.0
     alg = 0.0
-    cls_flops = {"xxt": 0.0, "square": 0.0, "rect": 0.0}
+    cls_flops = {"xxt": 0.0, "square": 0.0, "rect": 0.0, "small": 0.0}
     shapes = []
     for x in xs:
         b, r, c = x.shape
@@ -349,7 +352,7 @@ def run_case(name, steps, warmup, with_cpu, with_timing, with_extras=False):
         rec["ms_per_step_roofline_pass"] = events_ms
     if ktime is not None:
         per = {}
-        for k in ("normalize", "xxt", "square", "rect"):
+        for k in ("normalize", "xxt", "square", "rect", "small"):
             tot, cnt = probe[k]
             per[k] = {"total_ms": tot, "launches": cnt, "avg_us": 1e3 * tot / cnt if cnt else None}
         rec["kernels_one_step"] = per

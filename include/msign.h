@@ -360,19 +360,22 @@ const char* msign_version(void);
  * above is bracketed by a pair of events recorded on the call's stream;
  * msign_kernel_timing_read() waits for them, adds their durations to
  * per-class totals and clears the queue.
- * Classes: 0 = normalise (sum of squares + scale/cast) and the elementwise
- * passes of muon_step, 1 = X X^T (triangle),
+ * Classes: 0 = normalise (sum of squares + scale/cast) and the other
+ * elementwise passes, 1 = X X^T (triangle),
  * 2 = n x n triangle products (A^2 / Gram R, Q, Z, RZ updates), 3 = the
- * rectangular product (B X, Q X).
+ * rectangular product (B X, Q X), 4 = the whole-iteration kernel of small
+ * matrices (msign_ns with 64 < n <= 128 and m <= 256 after padding to 64,
+ * 16-bit products: every step in one launch, one workgroup per matrix).
  *   msign_kernel_timing_enable   mask of classes to time (bit k = class k,
  *                                MSIGN_KCLASS_ALL for all; a nonzero mask also
  *                                resets the totals); 0 disables (and frees
  *                                events).  Bits beyond the classes give
  *                                MSIGN_ERR_ARG.
- *   msign_kernel_timing_read     fills total_ms[4] and launches[4] (HOST).
+ *   msign_kernel_timing_read     fills total_ms[MSIGN_KCLASS_COUNT] and
+ *                                launches[MSIGN_KCLASS_COUNT] (HOST).
  */
-#define MSIGN_KCLASS_COUNT 4
-#define MSIGN_KCLASS_ALL 0xF
+#define MSIGN_KCLASS_COUNT 5
+#define MSIGN_KCLASS_ALL 0x1F
 msign_status_t msign_kernel_timing_enable(int32_t enable);
 msign_status_t msign_kernel_timing_read(double* total_ms, int64_t* launches);
 

@@ -23,7 +23,7 @@ _TORCH_TO_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "invalid dtype", 3: "invalid shape",
            4: "workspace", 5: "alias", 6: "HIP error"}
 MAX_STEPS = 64
-KCLASSES = ("normalize", "xxt", "square", "rect")
+KCLASSES = ("normalize", "xxt", "square", "rect", "small")
 
 
 class MsignError(RuntimeError):
@@ -445,7 +445,8 @@ def kernel_timing(enable: bool, classes=None):
 
 def read_kernel_timing():
     """{class: (total_ms, launches)} accumulated since timing was enabled."""
-    tot = (ctypes.c_double * 4)()
-    cnt = (ctypes.c_int64 * 4)()
+    k = len(KCLASSES)
+    tot = (ctypes.c_double * k)()
+    cnt = (ctypes.c_int64 * k)()
     _check(_load().msign_kernel_timing_read(tot, cnt))
-    return {KCLASSES[i]: (tot[i], cnt[i]) for i in range(4)}
+    return {KCLASSES[i]: (tot[i], cnt[i]) for i in range(k)}

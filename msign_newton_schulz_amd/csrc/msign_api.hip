@@ -28,6 +28,7 @@
 #include "launch.hpp"
 #include "mfma_probe.hpp"
 #include "normalize.hpp"
+#include "small_ns.hpp"
 
 #include <atomic>
 #include <cmath>
@@ -191,8 +192,8 @@ struct Timing {
   std::atomic<uint32_t> mask{0};  // classes being timed (bit k = class k)
   std::vector<Pending> pending;
   std::vector<hipEvent_t> pool;
-  double total_ms[MSIGN_KCLASS_COUNT] = {0, 0, 0, 0};
-  int64_t launches[MSIGN_KCLASS_COUNT] = {0, 0, 0, 0};
+  double total_ms[MSIGN_KCLASS_COUNT] = {};
+  int64_t launches[MSIGN_KCLASS_COUNT] = {};
 };
 
 Timing& timing() {
@@ -237,7 +238,7 @@ struct TimedLaunch {
   }
 };
 
-enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3 };
+enum KClass { KC_NORM = 0, KC_SYRK = 1, KC_SQUARE = 2, KC_RECT = 3, KC_SMALL = 4 };
 
 // --------------------------------------------------------------- launches --
 
@@ -706,8 +707,57 @@ size_t call_workspace(const msign_group_t* groups, int32_t ngroups, int32_t cdt,
 
 // The launches of standard NS over checked problems pr[0..ng), all of whose
 // products use compute dtype `cdt`, in a workspace laid out by plan_call.
+// The whole iteration of each matrix in one workgroup (small_ns_kernel),
+// for problems that fit it: 64 < n <= 128, m padded <= 256, 16-bit products.
+bool small_fits(const Prob& pr, int32_t cdt) {
+  return (cdt == MSIGN_BF16 || cdt == MSIGN_F16) && pr.s.np == kSmallN && pr.s.mp <= kSmallMaxM &&
+         pr.fuse == nullptr;
+}
+
+msign_status_t launch_small(const Prob& pr, int32_t io_dtype, int32_t cdt, int32_t steps, const float* coeffs,
+                            float eps, hipStream_t stream) {
+  SmallNsParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.x = pr.x;
+  q.y = pr.y;
+  q.rows = (int32_t)pr.rows;
+  q.cols = (int32_t)pr.cols;
+  q.n = (int32_t)pr.s.n;
+  q.m = (int32_t)pr.s.m;
+  q.mp = (int32_t)pr.s.mp;
+  q.tall = pr.s.tall ? 1 : 0;
+  q.io_dtype = io_dtype;
+  q.steps = steps;
+  q.eps = eps;
+  for (int t = 0; t < steps; ++t) coeff_at(coeffs, t, &q.abc[t][0], &q.abc[t][1], &q.abc[t][2]);
+  TimedLaunch tl(KC_SMALL, stream);
+  if (cdt == MSIGN_BF16)
+    small_ns_kernel<bf16_t><<<dim3((unsigned)pr.batch), kSmallThreads, 0, stream>>>(q);
+  else
+    small_ns_kernel<f16_t><<<dim3((unsigned)pr.batch), kSmallThreads, 0, stream>>>(q);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MSIGN_OK : hip_fail(e, "small_ns_kernel");
+}
+
 msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, int32_t steps, const float* coeffs,
                        float eps, bool improved, bool dense, void* workspace, hipStream_t stream) {
+  if (!improved && !dense) {
+    // small problems run alone in one launch each; the others go on below
+    Prob rest[MSIGN_MAX_GROUPS];
+    int nr = 0;
+    for (int i = 0; i < ng; ++i) {
+      if (small_fits(pr[i], cdt)) {
+        msign_status_t st = launch_small(pr[i], io_dtype, cdt, steps, coeffs, eps, stream);
+        if (st != MSIGN_OK) return st;
+      } else {
+        rest[nr++] = pr[i];
+      }
+    }
+    if (nr < ng) {
+      return nr == 0 ? MSIGN_OK
+                     : ns_exec(rest, nr, io_dtype, cdt, steps, coeffs, eps, improved, dense, workspace, stream);
+    }
+  }
   // symmetric n x n results: triangle products, or (dense) every tile with
   // the result stored through its transpose, the same matrix
   const ProductKind sym = dense ? DENSE : TRIANGLE;

@@ -180,7 +180,8 @@ def test_timing_read_rejects_null():
 
 def test_timing_mask_validation():
     lib = _lib()
-    assert lib.msign_kernel_timing_enable(0x10) == 1
+    assert lib.msign_kernel_timing_enable(0x20) == 1   # 5 classes: bits 0..4
+    assert lib.msign_kernel_timing_enable(0x10) == 0   # the small-matrix kernel only
     assert lib.msign_kernel_timing_enable(-1) == 1
     assert lib.msign_kernel_timing_enable(0b1000) == 0   # rect only
     assert lib.msign_kernel_timing_enable(0) == 0
