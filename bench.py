@@ -110,9 +110,10 @@ def elementwise_bytes(rows, cols, method, io_bytes, c_bytes):
     n, m = min(rows, cols), max(rows, cols)
     elems, padded = rows * cols, pad(n) * pad(m)
     x_bytes = 4 if method == "muon_ns" else io_bytes
-    if method in ("ns", "gram") and rows <= cols and cols % 64 == 0 and io_bytes == c_bytes:
-        return float(elems * x_bytes)
-    b = 2 * elems * x_bytes + padded * (c_bytes + (0 if method == "gram" else 4))
+    if method in ("ns", "gram", "ns_init") and rows <= cols and cols % 64 == 0 and io_bytes == c_bytes:
+        b = elems * x_bytes
+    else:
+        b = 2 * elems * x_bytes + padded * (c_bytes + (0 if method == "gram" else 4))
     if method == "ns_init":
         b += 3 * pad(n) * pad(n) * c_bytes
     if method == "muon_ns":

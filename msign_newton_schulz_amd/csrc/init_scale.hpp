@@ -13,9 +13,10 @@ namespace msign {
 // init_scale_kernel: one block per matrix adds that matrix's acc^2 slots of
 // the A A launch `q` (the slot layout of GemmParams::sumsq, `slots` per
 // tile, padding blocks of the folded triangle skipped) in a fixed order and
-// writes scales[4 bz + k] = s^-(1, 2, 4)[k].
+// writes scales[4 bz + k] = s^-(1, 2, 4)[k].  With `nscale` (the first
+// update reads the un-normalised input), scales[4 bz] is s^-1 nscale[4 bz + 1].
 __global__ void __launch_bounds__(256)
-init_scale_kernel(const GemmParams q, int32_t slots, float eps, float* scales) {
+init_scale_kernel(const GemmParams q, int32_t slots, float eps, float* scales, const float* nscale) {
   const int64_t b = blockIdx.x;
   const int tid = threadIdx.x;
   float acc = 0.f;
@@ -34,7 +35,7 @@ init_scale_kernel(const GemmParams q, int32_t slots, float eps, float* scales) {
     const float sum = ((ws[0] + ws[1]) + ws[2]) + ws[3];
     const float s = sqrtf(sqrtf(sqrtf(sum + eps)));
     const float r = 1.f / s;
-    scales[4 * b] = r;
+    scales[4 * b] = nscale != nullptr ? r * nscale[4 * b + 1] : r;
     scales[4 * b + 1] = r * r;
     scales[4 * b + 2] = (r * r) * (r * r);
     scales[4 * b + 3] = 0.f;

@@ -123,7 +123,7 @@ struct Prob {
 // the problem's own when it is alone, else one region shared by all.
 struct NsPlan {
   int32_t nblk;
-  size_t x32[2], xh[2], a, b, partial, sumsq, scales;
+  size_t x32[2], xh[2], a, b, partial, sumsq, scales, nscales;
 };
 
 struct GramPlan {
@@ -151,6 +151,7 @@ void plan_ns_regions(const Prob& pr, int32_t cdt, Carver& c, NsPlan& p) {
   p.partial = c.take((size_t)pr.batch * p.nblk * 4);
   p.sumsq = c.take(init_sumsq_floats(pr.s, pr.batch) * 4);
   p.scales = c.take((size_t)pr.batch * 4 * 4);
+  p.nscales = c.take((size_t)pr.batch * 4 * 4);
 }
 
 void plan_gram_regions(const Prob& pr, int32_t cdt, Carver& c, GramPlan& p) {
@@ -509,7 +510,8 @@ msign_status_t check_ws_alias(const void* x, size_t x_bytes, void* y, size_t y_b
 // those products' epilogues: 1/s^2 for the first X X^T and 1/s for the first
 // product with X (the rectangular step, or Gram's Q X), applied in fp32 to
 // the accumulated values.  Not with a fused Muon step (its input is the fp32
-// momentum) or the improved initial normalisation (its own first-step factor).
+// momentum).  With the improved initial normalisation, its first-step factor
+// for the update is multiplied by 1/s.
 bool direct_input(const Prob& pr, int32_t io_dtype, int32_t cdt) {
   return !pr.s.tall && io_dtype == cdt && pr.s.m % kPad == 0 && aligned(pr.x, 16) && pr.fuse == nullptr;
 }
@@ -769,8 +771,9 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
     Shape s;
     int64_t nm, nn;
     void *x32[2], *xh[2], *A, *B;
-    float *partial, *sumsq, *scales;
-    bool direct;  // the first products read the input (scales: 1/s^2, 1/s)
+    float *partial, *sumsq, *scales;  // scales: the improved initial normalisation's
+    float* nscales;  // 1/s^2, 1/s of a direct first step
+    bool direct;     // the first products read the input itself
   } gv[MSIGN_MAX_GROUPS];
   int64_t batches[MSIGN_MAX_GROUPS];
   for (int i = 0; i < ng; ++i) {
@@ -788,11 +791,12 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
     v.partial = reinterpret_cast<float*>(at(workspace, pl.partial));
     v.sumsq = reinterpret_cast<float*>(at(workspace, pl.sumsq));
     v.scales = reinterpret_cast<float*>(at(workspace, pl.scales));
+    v.nscales = reinterpret_cast<float*>(at(workspace, pl.nscales));
     batches[i] = pr[i].batch;
-    v.direct = !improved && direct_input(pr[i], io_dtype, cdt);
+    v.direct = direct_input(pr[i], io_dtype, cdt);
     if (v.direct) {
       st = launch_norm_scale(pr[i].x, io_dtype, pr[i].batch, pr[i].rows * pr[i].cols, v.partial, pl.nblk, eps,
-                             v.scales, stream);
+                             v.nscales, stream);
       if (st != MSIGN_OK) return st;
       continue;
     }
@@ -819,7 +823,7 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
         if (t == 0 && v.direct) {  // the input itself, n true rows, times 1/s^2
           const int64_t nm = v.s.n * v.s.m;
           qs[i] = gemm_base(pr[i].x, v.s.m, nm, pr[i].x, v.s.m, nm, v.s.n, v.s.n, v.s.mp, 1.f);
-          qs[i].vscale = v.scales;
+          qs[i].vscale = v.nscales;
         } else {
           qs[i] = gemm_base(v.xh[cur], v.s.mp, v.nm, v.xh[cur], v.s.mp, v.nm, v.s.np, v.s.np, v.s.mp, 1.f);
         }
@@ -853,8 +857,9 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
         q.tiles_n = used.tiles_n[i];
         q.tpm = used.tpm[i];
         TimedLaunch tl(KC_NORM, stream);
-        init_scale_kernel<<<dim3((unsigned)pr[i].batch), 256, 0, stream>>>(q, sumsq_slots_per_tile(used.bm), eps,
-                                                                           v.scales);
+        // a direct first step also folds its 1/s into the update's factor
+        init_scale_kernel<<<dim3((unsigned)pr[i].batch), 256, 0, stream>>>(
+            q, sumsq_slots_per_tile(used.bm), eps, v.scales, v.direct ? v.nscales : nullptr);
         e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e, "init_scale_kernel");
         const unsigned nb = (unsigned)((v.nn / 4 + 255) / 256);
@@ -890,7 +895,8 @@ msign_status_t ns_exec(const Prob* pr, int ng, int32_t io_dtype, int32_t cdt, in
           g = gemm_base(pr[i].x, v.s.m, nm, cubic ? v.A : v.B, v.s.np, v.nn, v.s.mp, v.s.n, v.s.np,
                         cubic ? b : 1.f);
           g.kvalid = (int32_t)v.s.n;
-          g.vscale = v.scales + 1;
+          // 1/s, or with the improved initial normalisation its factor times 1/s
+          g.vscale = rescale ? v.scales : v.nscales + 1;
           set_d(g, pr[i].x, v.s.m, nm, io_dtype, a, true);
         } else {
           g = gemm_base(v.xh[cur], v.s.mp, v.nm, cubic ? v.A : v.B, v.s.np, v.nn, v.s.mp, v.s.np, v.s.np,
