@@ -26,7 +26,8 @@
 // Accumulator layout of the 16x16 MFMA: lane l, register r holds
 // C[4 * (l / 16) + r][l % 16].
 //
-// The epilogue works in fp32 on the accumulator: alpha*acc + beta*D (D read
+// The epilogue works in fp32 on the accumulator: fma(alpha, acc, beta*D),
+// written out so that every epilogue path rounds alike (D read
 // through its transpose Dt[j][i], four consecutive values per lane), plus a
 // per-output diagonal term, then up to three stores of different dtype and
 // orientation (normal C[i][j] or transposed C[j][i]).
@@ -35,6 +36,7 @@
 #include "common.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace msign {
 
@@ -201,6 +203,27 @@ __device__ __forceinline__ int xcd_contiguous(int b, int nb) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + l;
 }
 
+// Wait for every load and LDS access of this wave, then the workgroup
+// barrier.  The wait is the compiler's own s_waitcnt (not inline asm), so
+// its waitcnt pass knows that nothing is in flight after it; the empty asm
+// before it keeps earlier memory accesses on its near side, the barrier's
+// asm keeps later ones after it.
+__device__ __forceinline__ void wait_all_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Tile coordinates of linear tile L over the batch: matrix bz, tile
 // (ti, tj).  Rectangular grids are walked in groups of GM tile rows, column
 // by column, so that concurrently running tiles share operand strips in L2.
@@ -253,7 +276,7 @@ __device__ __forceinline__ float epilogue_frag(const GemmParams& p, int64_t bz, 
   const int j = n0 + wn * WN + fn * 16 + (lane & 15);
   float v[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = p.alpha * a[r] + p.beta * d[r];
+  for (int r = 0; r < 4; ++r) v[r] = fmaf(p.alpha, a[r], p.beta * d[r]);
   if (p.vscale != nullptr) {
     const float f = p.vscale[4 * bz];
 #pragma unroll
@@ -363,14 +386,16 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, int64_t bz, i
   constexpr int FN = BN / WGN / 16;
   float d[NR * FN][4];
   epilogue_load_d<BM, BN, WGM, WGN, NR>(p, bz, ti, tj, wave, fm0, d);
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
+  // (compile-time loops: a runtime index into acc would put it in scratch)
+  static_for<NR>([&](auto K) {
+    constexpr int k = decltype(K)::value;
     sq[k] = 0.f;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+    static_for<FN>([&](auto FNI) {
+      constexpr int fn = decltype(FNI)::value;
       sq[k] += epilogue_frag<BM, BN, WGM, WGN, TRI>(p, bz, ti, tj, wave, fm0 + k, fn, acc[k * FN + fn],
                                                    d[k * FN + fn]);
-  }
+    });
+  });
 }
 
 // Sum of v over the wave (fixed butterfly, so bit-stable), stored by lane 0.
@@ -417,8 +442,8 @@ __device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz,
   const int wm = wave / WGN, wn = wave % WGN;
   float* st = stage + wave * (16 * PITCH);
   const float f = p.vscale != nullptr ? p.vscale[4 * bz] : 1.f;
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
+  static_for<FN>([&](auto FNI) {
+    constexpr int fn = decltype(FNI)::value;
     const int jf = n0 + wn * WN + fn * 16;  // first j of the group
     float d[FM][4];
 #pragma unroll
@@ -445,7 +470,7 @@ __device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz,
     for (int fm = 0; fm < FM; ++fm) {
       f32x4 v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (p.alpha * acc[fm][fn][r] + p.beta * d[fm][r]) * f;
+      for (int r = 0; r < 4; ++r) v[r] = fmaf(p.alpha, acc[fm][fn][r], p.beta * d[fm][r]) * f;
       *reinterpret_cast<f32x4*>(st + c * PITCH + fm * 16 + 4 * g) = v;
     }
 #pragma unroll
@@ -462,7 +487,7 @@ __device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz,
         out_vec4<true>(os, bz * os.bstride + (int64_t)j * os.ld + i, w);
       }
     }
-  }
+  });
   return true;
 }
 
@@ -479,7 +504,7 @@ __device__ __forceinline__ bool epilogue_staged_tri(const GemmParams& p, int64_t
                                                     int wave, float* stage) {
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
   constexpr int PITCH = 68;
-  static_assert(WM == 64 && WN == 64, "16 lanes x 4 values cover a row of the wave tile");
+  static_assert(WM == 64 && WN % 64 == 0, "16 lanes x 4 values cover a row of the wave tile");
   if (ti == tj || p.nout < 1) return false;
   const int m0 = ti * BM, n0 = tj * BN;
 #pragma unroll
@@ -496,52 +521,102 @@ __device__ __forceinline__ bool epilogue_staged_tri(const GemmParams& p, int64_t
   const int wm = wave / WGN, wn = wave % WGN;
   const int ib = m0 + wm * WM, jb = n0 + wn * WN;  // first row and column of the wave tile
   float* st = stage + wave * (16 * PITCH);
-  // finish four consecutive values of C along `along` at (r0, c0..c0+3),
-  // where D[r][c] = Dt[r ldd + c] by symmetry, and store them at
-  // ptr[r0 ld + c0] of every output
-  auto finish = [&](const f32x4& a, int r0, int c0) {
-    float d[4] = {0.f, 0.f, 0.f, 0.f};
-    if (has_d) load_vec4(p.Dt, bz * p.sd + (int64_t)r0 * p.ldd + c0, p.d_dtype, d);
-    float w[4];
+  // D is symmetric, so D[r][c] = Dt[r ldd + c].  D values are loaded ahead
+  // of the stores that need them, 16-bit D two groups (eight chunks of four
+  // values) at a time, fp32 D one group at a time: the compiler cannot tell
+  // D from the outputs, so a load placed after a store waits for it, and a
+  // load per chunk between the stores would wait out a memory round trip
+  // each time.  The D dtype is a template argument of the passes, so each
+  // form holds only its own registers (a whole pass's chunks at once spill
+  // in the 128-register budget).
+  const float f = p.vscale != nullptr ? p.vscale[4 * bz] : 1.f;
+  auto passes = [&](auto DKI) {
+    constexpr int DK = decltype(DKI)::value;  // 0: no D, 1: 16-bit, 2: fp32
+    constexpr int GA = DK == 2 ? 1 : 2;       // groups per D batch
+    using DV = typename std::conditional<DK == 2, f32x4, u32x2>::type;
+    auto d_at = [&](int r0, int c0) {
+      const int64_t idx = bz * p.sd + (int64_t)r0 * p.ldd + c0;
+      if constexpr (DK == 2) return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.Dt) + idx);
+      else if constexpr (DK == 1) return *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.Dt) + idx);
+      else return u32x2{0u, 0u};
+    };
+    // four consecutive values of C at (r0, c0 .. c0 + 3) from the staged
+    // accumulators a and the D chunk dv, stored at ptr[r0 ld + c0] of every
+    // output
+    auto finish = [&](const f32x4& a, const DV& dv, int r0, int c0) {
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DK == 1) {
+        const bool bf = p.d_dtype == DT_BF16;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = p.alpha * a[r] + p.beta * d[r];
-    if (p.vscale != nullptr) {
-      const float f = p.vscale[4 * bz];
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t hb = (uint16_t)(dv[r >> 1] >> (16 * (r & 1)));
+          d[r] = bf ? bf16_bits_to_f32(hb) : f16_bits_to_f32(hb);
+        }
+      } else if constexpr (DK == 2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] *= f;
-    }
+        for (int r = 0; r < 4; ++r) d[r] = dv[r];
+      }
+      float w[4];
 #pragma unroll
-    for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
-      if (o >= p.nout) break;
-      const OutSpec& os = p.out[o];
-      store_vec4(os.ptr, bz * os.bstride + (int64_t)r0 * os.ld + c0, os.dtype, w);
-    }
+      for (int r = 0; r < 4; ++r) w[r] = fmaf(p.alpha, a[r], p.beta * d[r]) * f;
+#pragma unroll
+      for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
+        if (o >= p.nout) break;
+        const OutSpec& os = p.out[o];
+        store_vec4(os.ptr, bz * os.bstride + (int64_t)r0 * os.ld + c0, os.dtype, w);
+      }
+    };
+    // mirror: column group fn staged as [j][i], rows j stored at ptr[j ld + i]
+    static_assert(FN % 2 == 0 && (FM * (FN / 4)) % 2 == 0, "groups go in pairs");
+    static_for<FN / GA>([&](auto PI) {
+      constexpr int fn0 = GA * decltype(PI)::value;
+      DV dv[4 * GA];
+#pragma unroll
+      for (int k = 0; k < 4 * GA; ++k) dv[k] = d_at(jb + (fn0 + k / 4) * 16 + 4 * (k % 4) + g, ib + 4 * c);
+#pragma unroll
+      for (int e = 0; e < GA; ++e) {
+        const int fn = fn0 + e;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          *reinterpret_cast<f32x4*>(st + c * PITCH + fm * 16 + 4 * g) = acc[fm][fn];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 4 * q + g;
+          finish(*reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c), dv[4 * e + q], jb + fn * 16 + row,
+                 ib + 4 * c);
+        }
+      }
+    });
+    // direct: row group fm staged as [i][j], 64 columns j at a time, rows i
+    // stored at ptr[i ld + j]
+    constexpr int NH = FN / 4;
+    static_for<FM * NH / GA>([&](auto PI) {
+      constexpr int fh0 = GA * decltype(PI)::value;
+      DV dv[4 * GA];
+#pragma unroll
+      for (int k = 0; k < 4 * GA; ++k) {
+        const int fh = fh0 + k / 4;
+        dv[k] = d_at(ib + (fh / NH) * 16 + 4 * (k % 4) + g, jb + 64 * (fh % NH) + 4 * c);
+      }
+#pragma unroll
+      for (int e = 0; e < GA; ++e) {
+        const int fm = (fh0 + e) / NH, h = (fh0 + e) % NH;
+#pragma unroll
+        for (int f4 = 0; f4 < 4; ++f4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st[(4 * g + r) * PITCH + f4 * 16 + c] = acc[fm][4 * h + f4][r];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 4 * q + g;
+          finish(*reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c), dv[4 * e + q], ib + fm * 16 + row,
+                 jb + 64 * h + 4 * c);
+        }
+      }
+    });
   };
-  // mirror: column group fn staged as [j][i], rows j stored at ptr[j ld + i]
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-      *reinterpret_cast<f32x4*>(st + c * PITCH + fm * 16 + 4 * g) = acc[fm][fn];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 4 * q + g;
-      finish(*reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c), jb + fn * 16 + row, ib + 4 * c);
-    }
-  }
-  // direct: row group fm staged as [i][j], rows i stored at ptr[i ld + j]
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st[(4 * g + r) * PITCH + fn * 16 + c] = acc[fm][fn][r];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = 4 * q + g;
-      finish(*reinterpret_cast<const f32x4*>(st + row * PITCH + 4 * c), ib + fm * 16 + row, jb + 4 * c);
-    }
-  }
+  if (!has_d) passes(std::integral_constant<int, 0>{});
+  else if (p.d_dtype == DT_F32) passes(std::integral_constant<int, 2>{});
+  else passes(std::integral_constant<int, 1>{});
   return true;
 }
 
@@ -553,7 +628,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
   if constexpr (!TRI && BM / WGM == 64) {
     if (stage != nullptr && epilogue_staged<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) return;
   }
-  if constexpr (TRI && BM / WGM == 64 && BN / WGN == 64) {
+  if constexpr (TRI && BM / WGM == 64 && (BN / WGN) % 64 == 0) {
     if (stage != nullptr && epilogue_staged_tri<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) {
       if (p.sumsq != nullptr) {  // acc^2 sums per fragment row, off-diagonal: counted twice
 #pragma unroll
@@ -574,8 +649,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
   // K-major A addressing) holds only one row's D values without spilling
   constexpr int NR = (FM >= 2 && (WGM * WGN < 16 || TRI)) ? 2 : 1;
   const float w2 = (TRI && ti != tj) ? 2.f : 1.f;
-#pragma clang loop unroll(full)
-  for (int fm0 = 0; fm0 < FM; fm0 += NR) {
+  static_for<FM / NR>([&](auto I) {
+    constexpr int fm0 = decltype(I)::value * NR;
     f32x4 rows[NR * FN];
 #pragma unroll
     for (int f = 0; f < NR * FN; ++f) rows[f] = acc[fm0 + f / FN][f % FN];
@@ -585,7 +660,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
 #pragma unroll
       for (int k = 0; k < NR; ++k) wave_sum_store(w2 * sq[k], sumsq_slot<BM, WGM, WGN>(p, L, wave, fm0 + k));
     }
-  }
+  });
 }
 
 // Block b of the launch of problem p (b counts from the problem's first
@@ -740,21 +815,55 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
   // Triangle products with direct loads and two MFMA sub-steps per slice
   // put the barrier between the sub-steps (measured on the 256 x 256 tier:
   // X X^T and A A 2.5-7 % faster, bit-identical; the rectangular product with
-  // its transpose reads gained nothing, and 14 % less in the unrolled form).
+  // its transpose reads gained nothing).
   constexpr bool DEFER = !AT && NST == 0 && KSUB == 2 && kAllFrags && KW == 1;
-  // A and B fragments of MFMA sub-step kk of the K slice in `stage`
-  // (row-major operands, all-fragments wave tiles; the deferred loop below)
+  // A fragments of MFMA sub-step kk of the K slice in `stage`
+  auto read_a = [&](const u32x4* stage, const int kk, u32x4 (&a)[FM]) {
+    const int ch = kk * 4 + (lane >> 4);
+    if constexpr (AT && ESZ == 2) {
+      // K rows 32 kk + 8 g + (r / 4) and that + 4, columns m .. m + 3 of
+      // the fragment's 16: after the transpose reads lane (g, r) holds
+      // column r at K = 32 kk + 8 g + 0..7, the order of the B fragment
+      const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int m = wm * WM + fm * 16 + 4 * (r & 3);
+        const int k0r = kk * 32 + 8 * g + (r >> 2), k1r = k0r + 4;
+        const int off0 = k0r * CPRA * 16 + swz_t<2, CPRA>(k0r, m >> 3) * 16 + (m & 7) * 2;
+        const int off1 = k1r * CPRA * 16 + swz_t<2, CPRA>(k1r, m >> 3) * 16 + (m & 7) * 2;
+        a[fm] = lds_read_tr16_pair(stage + kw * BM * CPR, off0, off1);
+      }
+    } else if constexpr (AT) {
+      // fp32: lane (g, r) reads column r at K = 16 kk + 4 g + 0..3
+      const int g = lane >> 4, r = lane & 15;
+      const float* base = reinterpret_cast<const float*>(stage + kw * BM * CPR);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int m = wm * WM + fm * 16 + r;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = kk * 16 + 4 * g + e;
+          v[e] = base[k * CPRA * 4 + swz_t<4, CPRA>(k, m >> 2) * 4 + (m & 3)];
+        }
+        a[fm] = __builtin_bit_cast(u32x4, v);
+      }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int row = wm * WM + fm * 16 + (lane & 15);
+        a[fm] = stage[(kw * BM + row) * CPR + swz<CPR>(row, ch)];
+      }
+    }
+  };
+  // A and B fragments of sub-step kk (all-fragments wave tiles)
   auto read_frags = [&](const u32x4* stage, const int kk, u32x4 (&a)[FM], u32x4 (&b)[FN]) {
     const int ch = kk * 4 + (lane >> 4);
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int row = wm * WM + fm * 16 + (lane & 15);
-      a[fm] = stage[row * CPR + swz<CPR>(row, ch)];
-    }
+    read_a(stage, kk, a);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int row = wn * WN + fn * 16 + (lane & 15);
-      b[fn] = stage[(BM + row) * CPR + swz<CPR>(row, ch)];
+      b[fn] = stage[(KW * BM + kw * BN + row) * CPR + swz<CPR>(row, ch)];
     }
   };
   // the sub-step's products, B fragment by B fragment (each B fragment is
@@ -773,41 +882,7 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
     for (int kk = 0; kk < KSUB; ++kk) {
       const int ch = kk * 4 + (lane >> 4);
       u32x4 a[FM];
-      if constexpr (AT && ESZ == 2) {
-        // K rows 32 kk + 8 g + (r / 4) and that + 4, columns m .. m + 3 of
-        // the fragment's 16: after the transpose reads lane (g, r) holds
-        // column r at K = 32 kk + 8 g + 0..7, the order of the B fragment
-        const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int m = wm * WM + fm * 16 + 4 * (r & 3);
-          const int k0r = kk * 32 + 8 * g + (r >> 2), k1r = k0r + 4;
-          const int off0 = k0r * CPRA * 16 + swz_t<2, CPRA>(k0r, m >> 3) * 16 + (m & 7) * 2;
-          const int off1 = k1r * CPRA * 16 + swz_t<2, CPRA>(k1r, m >> 3) * 16 + (m & 7) * 2;
-          a[fm] = lds_read_tr16_pair(stage + kw * BM * CPR, off0, off1);
-        }
-      } else if constexpr (AT) {
-        // fp32: lane (g, r) reads column r at K = 16 kk + 4 g + 0..3
-        const int g = lane >> 4, r = lane & 15;
-        const float* base = reinterpret_cast<const float*>(stage + kw * BM * CPR);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int m = wm * WM + fm * 16 + r;
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k = kk * 16 + 4 * g + e;
-            v[e] = base[k * CPRA * 4 + swz_t<4, CPRA>(k, m >> 2) * 4 + (m & 3)];
-          }
-          a[fm] = __builtin_bit_cast(u32x4, v);
-        }
-      } else {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int row = wm * WM + fm * 16 + (lane & 15);
-          a[fm] = stage[(kw * BM + row) * CPR + swz<CPR>(row, ch)];
-        }
-      }
+      read_a(stage, kk, a);
       if constexpr (kAllFrags) {
         u32x4 b[FN];
 #pragma unroll
@@ -882,53 +957,60 @@ __device__ __forceinline__ void gemm_nt_block(const GemmParams& p, const int b) 
                                                  0, 0, 0);
       }
     };
-    if constexpr (DEFER) {
-      // The barrier sits between a slice's two MFMA sub-steps.  Iteration j
-      // (slice j in stage j & 1, its sub-step-0 fragments already in
-      // registers): sub-step 0's products; sub-step 1's reads; wait for this
-      // wave's loads of slice j + 1 and its reads, barrier (slice j + 1 is
-      // then whole and stage j & 1 free); loads of slice j + 2 into stage
-      // j & 1; sub-step 1's products, whose fragments crossed the barrier in
-      // registers, so every wave has MFMAs to issue right after it while the
-      // reads of slice j + 1's sub-step 0 follow.  Two stages, one barrier
-      // per slice, as before.
-      static_assert(KSUB == 2 && kAllFrags && KW == 1, "deferred barrier layout");
-      u32x4 fa[FM], fb[FN];
-      // One iteration; `cur` holds slice j, `nxt` takes slice j + 1.
-      auto iter = [&](u32x4* cur, const u32x4* nxt, int j) {
-        mma_frags(fa, fb);
-        read_frags(cur, 1, fa, fb);
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (j + 2 < nk) issue(cur, (kt0 + j + 2) * KTE);
-        mma_frags(fa, fb);
-        if (j + 1 < nk) read_frags(nxt, 0, fa, fb);
-      };
-      // Two iterations per trip with both stages as non-aliasing pointers,
-      // so that no read waits for the loads in flight into the other stage.
-      auto trip = [&](u32x4* __restrict__ s0, u32x4* __restrict__ s1, int j) {
-        iter(s0, s1, j);
-        if (j + 1 < nk) iter(s1, s0, j + 1);
+    // In both loop forms slice s is loaded after barrier E(s - 1) into
+    // stage s & 1 (whose previous slice, s - 2, every wave finished reading
+    // before E(s - 1)), every loader waits for its loads before its next
+    // barrier, and slice s is read only after E(s).
+    auto plain_loop = [&]() {
+      // (one step: the loads into `wr` and the reads from `rd` are declared
+      // not to alias, so the reads need not wait for the loads in flight)
+      auto step = [&](const u32x4* __restrict__ rd, u32x4* __restrict__ wr, bool load_next, int k_next) {
+        if (load_next) issue(wr, k_next);
+        compute(rd);
       };
       if (nk > 0) issue(lds[0], kt0 * KTE);
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      if (nk > 1) issue(lds[1], (kt0 + 1) * KTE);
-      if (nk > 0) read_frags(lds[0], 0, fa, fb);
-      for (int j = 0; j < nk; j += 2) trip(lds[0], lds[1], j);
-      // the last barrier came after every read of the ring: it is free
-    } else {
-    // (one step: the loads into `wr` and the reads from `rd` are declared
-    // not to alias, so the reads need not wait for the loads in flight)
-    auto step = [&](const u32x4* __restrict__ rd, u32x4* __restrict__ wr, bool load_next, int k_next) {
-      if (load_next) issue(wr, k_next);
-      compute(rd);
+      for (int j = 0; j < nk; ++j) {
+        step(lds[j & 1], lds[(j + 1) & 1], j + 1 < nk, (kt0 + j + 1) * KTE);
+        wait_all_barrier();
+      }
     };
-    if (nk > 0) issue(lds[0], kt0 * KTE);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int j = 0; j < nk; ++j) {
-      step(lds[j & 1], lds[(j + 1) & 1], j + 1 < nk, (kt0 + j + 1) * KTE);
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    }
+    // The barrier between a slice's two MFMA sub-steps.  Iteration j (slice
+    // j in stage j & 1, its sub-step-0 fragments already in registers):
+    // sub-step 0's products; sub-step 1's reads; wait for this wave's loads
+    // of slice j + 1 and its reads, barrier E(j + 1); loads of slice j + 2
+    // into stage j & 1; sub-step 1's products, whose fragments crossed the
+    // barrier in registers, so the wave has MFMAs to issue right after it
+    // while the reads of slice j + 1's sub-step 0 follow.
+    auto deferred_loop = [&]() {
+      if constexpr (DEFER) {
+        u32x4 fa[FM], fb[FN];
+        // One iteration; `cur` holds slice j, `nxt` takes slice j + 1 (the
+        // two stages declared not to alias, so that no read waits for the
+        // loads in flight into the other stage).
+        auto iter = [&](u32x4* __restrict__ cur, const u32x4* __restrict__ nxt, int j) {
+          mma_frags(fa, fb);
+          read_frags(cur, 1, fa, fb);
+          wait_all_barrier();
+          if (j + 2 < nk) issue(cur, (kt0 + j + 2) * KTE);
+          mma_frags(fa, fb);
+          if (j + 1 < nk) read_frags(nxt, 0, fa, fb);
+        };
+        if (nk > 0) issue(lds[0], kt0 * KTE);
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (nk > 1) issue(lds[1], (kt0 + 1) * KTE);
+        if (nk > 0) read_frags(lds[0], 0, fa, fb);
+        // two iterations per trip (the one-iteration loop spills 32 bytes
+        // per lane)
+        for (int j = 0; j < nk; j += 2) {
+          iter(lds[0], lds[1], j);
+          if (j + 1 < nk) iter(lds[1], lds[0], j + 1);
+        }
+      }
+    };
+    if constexpr (DEFER) deferred_loop();
+    else plain_loop();
+    // the last barrier came after every read of the ring: it is free
   } else {
   // steps of KW slices; wave kw computes slice j * KW + kw of step j when
   // that slice is in range
