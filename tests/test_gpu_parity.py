@@ -69,6 +69,33 @@ def test_syrk_fused_epilogue(dt):
     assert torch.equal(c, c.transpose(-1, -2).contiguous())
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_syrk_fused_epilogue_big_tiles(dt):
+    """C = alpha X X^T + beta D + gamma I on 256 x 256 tiles (5800 x 5800:
+    276 triangle tiles, the last row and column ragged), so the staged
+    epilogue of the off-diagonal tiles adds D loaded ahead of its stores, in
+    each D dtype; element-wise within the product's error bound, bitwise
+    symmetric."""
+    M = require_gpu()
+    announce(f"syrk epilogue 256-tiles dt={dt}")
+    n, k = 5800, 320
+    x = _input(n, k, dt, 4242)
+    d0 = _input(n, n, dt, 4243)
+    d = ((d0.float() + d0.float().transpose(-1, -2)) * 0.5).to(TORCH_DT[dt])  # symmetric
+    del d0
+    alpha, beta, gamma = 0.75, -1.5, 2.25
+    c = M.syrk_xxt(x.cuda(), alpha=alpha, d=d.cuda(), beta=beta, gamma=gamma)
+    torch.cuda.synchronize()
+    xx, dd = f64(x)[0], f64(d)[0]
+    ref = alpha * (xx @ xx.T) + beta * dd + gamma * np.eye(n)
+    ax = np.abs(xx)
+    scale = abs(alpha) * (ax @ ax.T) + abs(beta) * np.abs(dd) + abs(gamma)
+    u = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11, "f32": 2.0 ** -22}[dt]
+    err = np.abs(f64(c)[0] - ref) / (scale * (u + 2 * k * 2.0 ** -24))
+    assert float(err.max()) <= 1.0, float(err.max())
+    assert torch.equal(c, c.transpose(-1, -2).contiguous()), "C must be bitwise symmetric"
+
+
 @pytest.mark.parametrize("n,k,batch", [(100, 300, 2), (1536, 1024, 2), (2048, 2048, 4)])
 def test_syrk_full_tiles_comparator(n, k, batch):
     """The full-tile comparator (every tile of X X^T, the three tile tiers)
