@@ -366,6 +366,33 @@ def test_ns_improved_init(rows, cols, batch, cdt, tol):
         assert O.max_rel_fro_error(f64(y_plain[i]), ref) > 2 * max(err, tol / 10)
 
 
+@pytest.mark.parametrize("where", ["first", "every"])
+@pytest.mark.parametrize("method,io,cdt,tol", [("ns", "bf16", "bf16", 2e-2), ("ns", "f32", "f32", 1e-4),
+                                               ("gram", "bf16", "f16", 2e-2)])
+def test_safety_factor_as_scaled_coefficients(where, method, io, cdt, tol):
+    """The safety factor of "Gram Newton-Schulz" §3.3 (formula lost in the
+    text) in either plain reading is a per-step table with rows
+    (a / s, b / s^3, c / s^5): the first row (X_0 divided by s) or every row.
+    The library takes it as any other table; checked against the oracle."""
+    M = require_gpu()
+    announce(f"safety factor {where} {method} {cdt}")
+    s = 1.05
+    a, b, c = O.KELLER_ABC
+    scaled = [a / s, b / s ** 3, c / s ** 5]
+    table = [scaled] + [[a, b, c]] * 4 if where == "first" else [scaled] * 5
+    x = _input(192, 640, io, 808, batch=2, noise=0.02, spike=4)
+    if method == "ns":
+        y = M.msign_ns(x.cuda(), steps=5, coeffs=table, compute_dtype=TORCH_DT[cdt])
+    else:
+        y = M.msign_gram_ns(x.cuda(), steps=5, coeffs=table, compute_dtype=TORCH_DT[cdt], restart_after=(2,))
+    torch.cuda.synchronize()
+    ref = O.ns(f64(x), coeffs=np.array(table), steps=5)
+    err = O.max_rel_fro_error(f64(y), ref)
+    assert err <= tol, err
+    # the result follows the table: the plain iteration is much further away
+    assert O.max_rel_fro_error(f64(y), O.ns(f64(x))) > 2 * err
+
+
 def test_ns_improved_init_with_cubic_first_step():
     M = require_gpu()
     announce("msign_ns improved init, cubic table")

@@ -154,6 +154,37 @@ def test_ns_equals_per_singular_value_composition(shape, table):
     assert np.allclose(O.ns_single(m, rows, t), O.spectral_ns_single(m, rows, t), atol=1e-12)
 
 
+@pytest.mark.parametrize("where", ["first", "every"])
+def test_safety_factor_as_scaled_coefficients(where):
+    # "Gram Newton-Schulz" §3.3 asks for a safety factor so that singular
+    # values up to 1.05 still converge; its formula is lost in the text.
+    # Both plain readings are per-step tables: dividing X_0 by s is the first
+    # step's polynomial taken at x / s, i.e. (a / s, b / s^3, c / s^5); taking
+    # every step's polynomial at x / s scales every row.  Checked against the
+    # SVD route, where the singular values are divided by s directly.
+    s = 1.05
+    a, b, c = O.KELLER_ABC
+    scaled = (a / s, b / s ** 3, c / s ** 5)
+    table = [scaled] + [(a, b, c)] * 4 if where == "first" else [scaled] * 5
+    m = _rand((12, 40), 77, 2.0)
+    u, sv, vt = np.linalg.svd(m, full_matrices=False)
+    y = sv / math.sqrt(float(np.sum(sv * sv)) + O.DEFAULT_EPS)
+    for t in range(5):
+        z = y / s if (t == 0 or where == "every") else y
+        y = a * z + b * z ** 3 + c * z ** 5
+    expect = (u * y) @ vt
+    assert np.allclose(O.ns_single(m, table, 5), expect, atol=1e-12)
+    assert np.allclose(O.gram_ns_single(m, table, 5, restart_after=(2,)), expect, atol=1e-12)
+    # a singular value pushed to 1.05 by an error of the normalisation is
+    # mapped as 1.0 is without the factor (first-step reading)
+    if where == "first":
+        def comp(x, rows):
+            for ra, rb, rc in rows:
+                x = ra * x + rb * x ** 3 + rc * x ** 5
+            return x
+        assert comp(1.05, table) == pytest.approx(comp(1.0, [(a, b, c)] * 5), abs=1e-14)
+
+
 @pytest.mark.parametrize("table", ["bernstein_cubic", "nil9_cubic"])
 def test_cubic_tables_fix_one(table):
     # nil9.net, third-order iteration: f(1) = a + b = 1 and |f'(1)| = |a + 3b| < 1
