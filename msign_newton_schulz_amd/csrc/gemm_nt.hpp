@@ -6,7 +6,8 @@
 // along K.  Every product of the method is brought to this form:
 //   X X^T                  P = Q = X                    ("Newton-Schulz" A)
 //   c A A + b A            P = Q = A, D = A             (A is symmetric)
-//   B X + a X              P = B, Q = X^T, D = X        (rectangular step)
+//   B X + a X              computed as X^T B + a X^T: P = X read K-major
+//                          (AT), Q = B (symmetric), D = X, stored transposed
 //   Gram R R, Q Z, R Z ... P, Q symmetric, so Q^T = Q
 // The n x n products are symmetric, so in triangle mode (TRI) only tiles with
 // ti <= tj are launched; each is stored normally and its transpose is stored
@@ -16,10 +17,12 @@
 // C <- aAB + bC + gI).  In a diagonal tile only elements with i <= j are
 // kept, so C is bitwise symmetric.
 //
-// Data path: 16-byte global loads of 128-byte K slices into registers, then
-// into a double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by
-// row (conflict-free ds_read_b128 for the MFMA fragments); one barrier per
-// K slice.  bf16/f16 use v_mfma_f32_16x16x32_{bf16,f16} (one 16-byte fragment
+// Data path: 128-byte (256 x 256 tiles) or 64-byte (128 x 128) K slices go
+// from global memory straight into a double-buffered LDS tile (buffer_load
+// ... lds); the 64 x 64 tier stages them through registers.  The tile's
+// 16-byte chunks are XOR-swizzled by row (conflict-free ds_read_b128 for the
+// MFMA fragments; K-major operands are read back with ds_read_b64_tr_b16);
+// one barrier per K slice.  bf16/f16 use v_mfma_f32_16x16x32_{bf16,f16} (one 16-byte fragment
 // per lane per MFMA); fp32 uses v_mfma_f32_16x16x4_f32, four per fragment.
 // The K order inside a fragment is the same for both operands, so the
 // product does not depend on the hardware's K lane assignment.

@@ -11,10 +11,10 @@
 // the A = X X^T reuse of the flash-muon excerpt on nil9.net), per step:
 //   A  = X X^T                 triangle product, K = m
 //   B  = c A A + b A           triangle product, K = n, D = A
-//   X' = B X + a X             full product, Q operand = X^T, D = X (fp32)
-// X is carried in fp32 between steps (X32t, stored transposed so the
-// epilogue reads four consecutive values per lane), together with two
-// compute-dtype copies that feed the products: Xh (n x m) and Xht (m x n).
+//   X' = B X + a X             rectangular product, computed as X^T B + a X^T
+//                              with X read K-major, D = X (fp32)
+// X is carried in fp32 between steps (X32, n x m), together with a
+// compute-dtype copy Xh (n x m) that feeds the products (both ping-pong).
 // Rounding only the product operands, not the iterate, keeps the small
 // singular directions of spiked (momentum-like) matrices intact.
 //
