@@ -416,8 +416,9 @@ def extras(M, x, out, ns_ms):
     """Comparisons the headline workload's line carries (a few seconds):
     - syrk_unit: X X^T at 8192^2 bf16 by the triangle kernel (upper tiles,
       mirrored), by the same kernel on every tile, and by torch.matmul
-      (hipBLASLt), as in the flash-muon excerpt on nil9.net (its symmetric
-      operator at dimension 8192 takes about half the native time);
+      (hipBLASLt) of x and x.T, as in the flash-muon excerpt on nil9.net
+      (its symmetric operator at dimension 8192 takes about half the
+      native time), also with x.T copied to row-major first;
     - dense_products_ns: the same NS with X X^T and c A A + b A on every
       tile, the end-to-end saving of the symmetric products (the excerpt:
       0.71x of native NS time);
@@ -433,13 +434,19 @@ def extras(M, x, out, ns_ms):
     c = torch.empty((1, x.shape[1], x.shape[1]), dtype=x.dtype, device=x.device)
     t_tri = time_calls(lambda: M.syrk_xxt(x0, out=c), 10)
     t_full = time_calls(lambda: M.syrk_xxt(x0, out=c, full_tiles=True), 10)
+    # the library product as the excerpt names it, matmul(x, x.T) (2-D, the
+    # transposed operand as a view), and with X^T copied first (row-major
+    # operands); the library picks a kernel on its first calls, so these
+    # get more warm-up calls
     xm, xt = x0[0], x0[0].transpose(0, 1).contiguous()
     cm = c[0]
-    t_torch = time_calls(lambda: torch.matmul(xm, xt, out=cm), 10)
+    t_torch = time_calls(lambda: torch.matmul(xm, xm.t(), out=cm), 10, warmup=5)
+    t_torch_nn = time_calls(lambda: torch.matmul(xm, xt, out=cm), 10, warmup=5)
     n, k = x.shape[1], x.shape[2]
     res["syrk_unit"] = {
         "shape": [int(n), int(k)], "dtype": "bf16",
         "triangle_us": 1e3 * t_tri, "full_tiles_us": 1e3 * t_full, "torch_matmul_us": 1e3 * t_torch,
+        "torch_matmul_row_major_operands_us": 1e3 * t_torch_nn,
         "triangle_over_full_tiles": t_tri / t_full, "triangle_over_torch_matmul": t_tri / t_torch,
         "triangle_algorithmic_tflops": float(k) * n * n / (t_tri * 1e-3) / 1e12,
         "context": "flash-muon excerpt (nil9.net): about 0.5x of native matmul at dimension 8192, "
