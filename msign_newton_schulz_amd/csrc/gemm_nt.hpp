@@ -499,8 +499,9 @@ __device__ __forceinline__ bool epilogue_staged(const GemmParams& p, int64_t bz,
 // passes through the wave's LDS region: 16-column groups read back by rows
 // give the mirror stores, 16-row groups read back by rows the direct ones.
 // D (symmetric, as every D of a triangle product is) is added after the
-// read-back, loaded by rows too.  Diagonal tiles (masking, diagonal terms)
-// return false.
+// read-back, loaded by rows too.  In a diagonal tile only the waves wholly
+// above the diagonal (all i < j) qualify; the others (masking, diagonal
+// terms) return false.
 template <int BM, int BN, int WGM, int WGN>
 __device__ __forceinline__ bool epilogue_staged_tri(const GemmParams& p, int64_t bz, int ti, int tj,
                                                     const f32x4 (&acc)[BM / WGM / 16][BN / WGN / 16],
@@ -508,7 +509,8 @@ __device__ __forceinline__ bool epilogue_staged_tri(const GemmParams& p, int64_t
   constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
   constexpr int PITCH = 68;
   static_assert(WM == 64 && WN % 64 == 0, "16 lanes x 4 values cover a row of the wave tile");
-  if (ti == tj || p.nout < 1) return false;
+  // a diagonal tile qualifies only for the waves wholly above its diagonal
+  if (p.nout < 1 || (ti == tj && wave / WGN >= wave % WGN)) return false;
   const int m0 = ti * BM, n0 = tj * BN;
 #pragma unroll
   for (int o = 0; o < MSIGN_MAX_OUT; ++o) {
@@ -632,18 +634,30 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int L, int64_t bz,
     if (stage != nullptr && epilogue_staged<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) return;
   }
   if constexpr (TRI && BM / WGM == 64 && (BN / WGN) % 64 == 0) {
-    if (stage != nullptr && epilogue_staged_tri<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) {
-      if (p.sumsq != nullptr) {  // acc^2 sums per fragment row, off-diagonal: counted twice
+    // acc^2 sums per fragment row (off-diagonal tiles counted twice, for
+    // their mirror)
+    auto sums = [&]() {
+      if (p.sumsq == nullptr) return;
+      const float w = ti != tj ? 2.f : 1.f;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          float sq = 0.f;
+      for (int fm = 0; fm < FM; ++fm) {
+        float sq = 0.f;
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
+        for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sq += acc[fm][fn][r] * acc[fm][fn][r];
-          wave_sum_store(2.f * sq, sumsq_slot<BM, WGM, WGN>(p, L, wave, fm));
-        }
+          for (int r = 0; r < 4; ++r) sq += acc[fm][fn][r] * acc[fm][fn][r];
+        wave_sum_store(w * sq, sumsq_slot<BM, WGM, WGN>(p, L, wave, fm));
       }
+    };
+    // In a diagonal tile the waves wholly below the diagonal store nothing:
+    // every element there is the mirror of one above it (i > j), which the
+    // waves above the diagonal store.
+    if (ti == tj && wave / WGN > wave % WGN) {
+      sums();
+      return;
+    }
+    if (stage != nullptr && epilogue_staged_tri<BM, BN, WGM, WGN>(p, bz, ti, tj, acc, wave, stage)) {
+      sums();
       return;
     }
   }
