@@ -163,6 +163,8 @@ NS_CASES = [
     (65, 300, "bf16", "bf16", 1),   # n = 65, the smallest bf16-product size
     (96, 160, "f16", "bf16", 3),
     (300, 520, "f32", "f32", 1),
+    (100, 130, "f32", "f32", 2),    # fp32 products, ragged both ways
+    (256, 128, "f32", "f32", 1),    # fp32 products, tall
 ]
 
 
